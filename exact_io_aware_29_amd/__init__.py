@@ -1,0 +1,174 @@
+"""Exact IO-aware attention for MI355X (gfx950): Python binding of ``libfa.so``.
+
+The functions here carry the names of the C entry points in ``include/fa.h``
+and only marshal arguments: they read shapes and strides off torch tensors,
+allocate outputs with torch (device memory and streams are the only things
+torch provides), and call the HIP library on the current torch stream. Every
+step of the computation runs in the library's kernels; there is no CPU or
+PyTorch fallback, and a missing library raises.
+
+Tensor layout: [batch, heads, seqlen, head_dim] with unit stride along
+head_dim (any other strides that are multiples of 16 bytes work).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from . import _abi
+from ._abi import FA_BF16, FA_FP32, FA_MASK_BLOCK, Params, Strides  # noqa: F401
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_tile_log_words", "fa_strerror",
+           "FAError", "make_params", "library"]
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _abi.load()
+        self.status = status
+        detail = lib.fa_last_error_detail().decode()
+        super().__init__(f"{where}: {lib.fa_strerror(status).decode()} (status {status})"
+                         + (f": {detail}" if detail else ""))
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    return _abi.load()
+
+
+def fa_strerror(status: int) -> str:
+    return _abi.load().fa_strerror(status).decode()
+
+
+_DT = {torch.bfloat16: FA_BF16, torch.float32: FA_FP32}
+
+
+def _strides(t: torch.Tensor) -> Strides:
+    if t.dim() != 4:
+        raise ValueError("tensors must be 4-D [batch, heads, seqlen, head_dim]")
+    if t.stride(3) != 1:
+        raise ValueError("head_dim must have unit stride")
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def make_params(*, dtype=FA_BF16, o_dtype=None, batch, heads_q, heads_kv, seqlen, head_dim,
+                scale=None, causal=False, seqlens_k=0, block_mask=0, block_mask_ld=0) -> Params:
+    """fa_params from plain values (device pointers as ints)."""
+    return Params(dtype, dtype if o_dtype is None else o_dtype, batch, heads_q, heads_kv, seqlen,
+                  head_dim, 1.0 / math.sqrt(head_dim) if scale is None else scale, int(bool(causal)),
+                  seqlens_k or None, block_mask or None, block_mask_ld)
+
+
+def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype) -> Params:
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if k.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("k/v shape does not match q")
+    bm_ptr, bm_ld = 0, 0
+    if block_mask is not None:
+        if block_mask.dtype != torch.uint8 or block_mask.dim() != 2 or block_mask.stride(1) != 1:
+            raise ValueError("block_mask must be a 2-D uint8 tensor with unit column stride")
+        if block_mask.shape[0] < -(-N // FA_MASK_BLOCK):
+            raise ValueError("block_mask has too few rows")
+        bm_ptr, bm_ld = block_mask.data_ptr(), block_mask.stride(0)
+    sl_ptr = 0
+    if seqlens_k is not None:
+        if seqlens_k.dtype != torch.int32 or seqlens_k.numel() < B or not seqlens_k.is_contiguous():
+            raise ValueError("seqlens_k must be a contiguous int32 tensor of length >= batch")
+        sl_ptr = seqlens_k.data_ptr()
+    odt = _DT[q.dtype] if o_dtype is None else _DT[o_dtype]
+    return make_params(dtype=_DT[q.dtype], o_dtype=odt, batch=B, heads_q=Hq, heads_kv=k.shape[1],
+                       seqlen=N, head_dim=d, scale=scale, causal=causal, seqlens_k=sl_ptr,
+                       block_mask=bm_ptr, block_mask_ld=bm_ld)
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def fa_tile_log_words(params: Params) -> int:
+    return _abi.load().fa_tile_log_words(ctypes.byref(params))
+
+
+def fa_bwd_workspace_size(params: Params) -> int:
+    return _abi.load().fa_bwd_workspace_size(ctypes.byref(params))
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+           causal: bool = False, seqlens_k: Optional[torch.Tensor] = None,
+           block_mask: Optional[torch.Tensor] = None, o_dtype: Optional[torch.dtype] = None,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           tile_log: bool = False):
+    """Forward pass. Returns (O, LSE, tile_log or None)."""
+    lib = _abi.load()
+    p = _params_from(q, k, scale=scale, causal=causal, seqlens_k=seqlens_k,
+                     block_mask=block_mask, o_dtype=o_dtype)
+    B, Hq, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.numel() != B * Hq * N:
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    log = None
+    if tile_log:
+        log = torch.zeros(lib.fa_tile_log_words(ctypes.byref(p)), dtype=torch.int32,
+                          device=q.device)
+    st = lib.fa_fwd(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                    _strides(v), _ptr(out), _strides(out), _ptr(lse), _ptr(log), _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd")
+    return out, lse, log
+
+
+def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+           dout: torch.Tensor, *, scale: Optional[float] = None, causal: bool = False,
+           seqlens_k: Optional[torch.Tensor] = None, block_mask: Optional[torch.Tensor] = None,
+           dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+           dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           tile_log: bool = False, stage_events: Optional[Sequence] = None):
+    """Backward pass. Returns (dQ, dK, dV, tile_log or None).
+
+    ``stage_events``: optional 4 ``torch.cuda.Event`` objects, recorded by
+    the library around its three kernels (for per-kernel timing).
+    """
+    lib = _abi.load()
+    p = _params_from(q, k, scale=scale, causal=causal, seqlens_k=seqlens_k,
+                     block_mask=block_mask, o_dtype=o.dtype)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = lib.fa_bwd_workspace_size(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(need // 4 + 4, dtype=torch.float32, device=q.device)
+    log = None
+    if tile_log:
+        log = torch.zeros(2 * lib.fa_tile_log_words(ctypes.byref(p)), dtype=torch.int32,
+                          device=q.device)
+    ev_arr = None
+    if stage_events is not None:
+        handles = []
+        for ev in stage_events:
+            if ev.cuda_event == 0:
+                ev.record()  # materialise the underlying hipEvent_t
+            handles.append(ev.cuda_event)
+        ev_arr = (ctypes.c_void_p * 4)(*handles)
+    st = lib.fa_bwd(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                    _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
+                    _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
+                    _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(log),
+                    ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
+                    _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv, log

@@ -1,0 +1,238 @@
+// fa_api.cpp -- C ABI entry points: host-side validation, then kernel launch.
+//
+// Every check runs on the host before the first HIP call, so an invalid call
+// returns a status code without touching the GPU (and can be tested on a
+// machine without one).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+size_t elem_size(int dtype) { return dtype == FA_BF16 ? 2 : 4; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_params(const fa_params* p) {
+  if (!p) return fail(FA_ERR_NULL, "params is NULL");
+  if (p->dtype != FA_BF16 && p->dtype != FA_FP32)
+    return fail(FA_ERR_DTYPE, "dtype %d is not FA_BF16 or FA_FP32", p->dtype);
+  if (p->o_dtype != FA_BF16 && p->o_dtype != FA_FP32)
+    return fail(FA_ERR_DTYPE, "o_dtype %d is not FA_BF16 or FA_FP32", p->o_dtype);
+  if (p->dtype == FA_FP32 && p->o_dtype != FA_FP32)
+    return fail(FA_ERR_DTYPE, "fp32 inputs need an fp32 output");
+  if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->seqlen <= 0)
+    return fail(FA_ERR_SHAPE, "batch, heads and seqlen must be positive");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(FA_ERR_HEADDIM, "head_dim %d is not 64 or 128", p->head_dim);
+  if (p->heads_q % p->heads_kv != 0)
+    return fail(FA_ERR_GQA, "heads_q %d is not a multiple of heads_kv %d", p->heads_q, p->heads_kv);
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f))
+    return fail(FA_ERR_SCALE, "scale must be finite and positive");
+  if (p->seqlen > (1 << 30)) return fail(FA_ERR_SHAPE, "seqlen above 2^30");
+  const int64_t blocks = ceil_div(p->seqlen, 128);
+  const int64_t grid_q = blocks * p->heads_q * p->batch;
+  if (grid_q >= (int64_t(1) << 31) || (int64_t)p->batch * p->heads_q * p->seqlen >= (int64_t(1) << 40))
+    return fail(FA_ERR_SHAPE, "problem too large to index");
+  if (p->block_mask && p->block_mask_ld < blocks)
+    return fail(FA_ERR_MASK, "block_mask_ld %d < ceil(seqlen/128) = %lld", p->block_mask_ld,
+                (long long)blocks);
+  return FA_OK;
+}
+
+int check_tensor(const char* name, const void* ptr, fa_strides s, int dtype) {
+  if (!ptr) return fail(FA_ERR_NULL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+    return fail(FA_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  const int64_t q = 16 / (int64_t)elem_size(dtype);
+  if (s.batch < 0 || s.head < 0 || s.row < 0 || s.batch % q || s.head % q || s.row % q)
+    return fail(FA_ERR_STRIDE, "%s strides must be >= 0 and multiples of 16 bytes", name);
+  return FA_OK;
+}
+
+fa::Problem make_problem(const fa_params* p) {
+  fa::Problem pr;
+  pr.B = p->batch;
+  pr.Hq = p->heads_q;
+  pr.Hkv = p->heads_kv;
+  pr.N = p->seqlen;
+  pr.G = p->heads_q / p->heads_kv;
+  pr.scale = p->scale;
+  pr.scale_l2 = p->scale * 1.4426950408889634f;
+  pr.causal = p->causal != 0;
+  pr.seqlens = p->seqlens_k;
+  pr.bm = p->block_mask;
+  pr.bm_ld = p->block_mask_ld;
+  pr.nlb = (int)ceil_div(p->seqlen, 128);
+  pr.logw = (int)ceil_div(pr.nlb, 32);
+  return pr;
+}
+
+fa::Strides conv(fa_strides s) { return fa::Strides{s.batch, s.head, s.row}; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FA_CHECK(expr)            \
+  do {                            \
+    const int st_ = (expr);       \
+    if (st_ != FA_OK) return st_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_tile_log_words(const fa_params* p) {
+  if (check_params(p) != FA_OK) return 0;
+  const int64_t nlb = ceil_div(p->seqlen, 128);
+  return (size_t)p->batch * p->heads_q * nlb * ceil_div(nlb, 32);
+}
+
+size_t fa_bwd_workspace_size(const fa_params* p) {
+  if (check_params(p) != FA_OK) return 0;
+  return (size_t)p->batch * p->heads_q * p->seqlen * sizeof(float);
+}
+
+int fa_fwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+           const void* v, fa_strides sv, void* o, fa_strides so, float* lse, uint32_t* tile_log,
+           void* stream) {
+  g_detail[0] = '\0';
+  FA_CHECK(check_params(p));
+  FA_CHECK(check_tensor("q", q, sq, p->dtype));
+  FA_CHECK(check_tensor("k", k, sk, p->dtype));
+  FA_CHECK(check_tensor("v", v, sv, p->dtype));
+  FA_CHECK(check_tensor("o", o, so, p->o_dtype));
+  if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
+  if (tile_log && reinterpret_cast<uintptr_t>(tile_log) % 4)
+    return fail(FA_ERR_ALIGN, "tile_log is not 4-byte aligned");
+
+  fa::FwdArgs a;
+  a.p = make_problem(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.sq = conv(sq);
+  a.sk = conv(sk);
+  a.sv = conv(sv);
+  a.so = conv(so);
+  a.lse = lse;
+  a.log = tile_log;
+  a.o_fp32 = p->o_dtype == FA_FP32;
+  const hipError_t e =
+      fa::launch_fwd(a, p->dtype == FA_BF16 ? 0 : 1, p->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return FA_OK;
+}
+
+int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+           const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,
+           fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk, fa_strides sdk,
+           void* dv, fa_strides sdv, void* workspace, size_t workspace_bytes, uint32_t* tile_log,
+           void* const* stage_events, void* stream) {
+  g_detail[0] = '\0';
+  FA_CHECK(check_params(p));
+  if (p->dtype != FA_BF16) return fail(FA_ERR_DTYPE, "the backward pass supports bf16 inputs only");
+  FA_CHECK(check_tensor("q", q, sq, p->dtype));
+  FA_CHECK(check_tensor("k", k, sk, p->dtype));
+  FA_CHECK(check_tensor("v", v, sv, p->dtype));
+  FA_CHECK(check_tensor("o", o, so, p->o_dtype));
+  FA_CHECK(check_tensor("dout", dout, sdo, p->dtype));
+  FA_CHECK(check_tensor("dq", dq, sdq, p->dtype));
+  FA_CHECK(check_tensor("dk", dk, sdk, p->dtype));
+  FA_CHECK(check_tensor("dv", dv, sdv, p->dtype));
+  if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
+  const size_t need = fa_bwd_workspace_size(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(FA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (tile_log && reinterpret_cast<uintptr_t>(tile_log) % 4)
+    return fail(FA_ERR_ALIGN, "tile_log is not 4-byte aligned");
+  if (stage_events)
+    for (int i = 0; i < 4; ++i)
+      if (!stage_events[i]) return fail(FA_ERR_NULL, "stage_events[%d] is NULL", i);
+
+  fa::BwdArgs a;
+  a.p = make_problem(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.sq = conv(sq);
+  a.sk = conv(sk);
+  a.sv = conv(sv);
+  a.so = conv(so);
+  a.sdo = conv(sdo);
+  a.sdq = conv(sdq);
+  a.sdk = conv(sdk);
+  a.sdv = conv(sdv);
+  a.lse = lse;
+  a.dvec = static_cast<float*>(workspace);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const size_t words = fa_tile_log_words(p);
+  a.log_kv = tile_log;
+  a.log_q = tile_log ? tile_log + words : nullptr;
+  a.o_fp32 = p->o_dtype == FA_FP32;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) : hipSuccess;
+  };
+  hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = fa::launch_bwd_pre(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_pre launch");
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = fa::launch_bwd_dkdv(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_dkdv launch");
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = fa::launch_bwd_dq(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_dq launch");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event record");
+  return FA_OK;
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid or too large problem size";
+    case FA_ERR_DTYPE: return "unsupported dtype combination";
+    case FA_ERR_HEADDIM: return "head_dim must be 64 or 128";
+    case FA_ERR_GQA: return "heads_q must be a multiple of heads_kv";
+    case FA_ERR_STRIDE: return "strides must be non-negative multiples of 16 bytes";
+    case FA_ERR_ALIGN: return "pointer not sufficiently aligned";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_MASK: return "block_mask_ld smaller than the number of 128-key blocks";
+    case FA_ERR_SCALE: return "scale must be finite and positive";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

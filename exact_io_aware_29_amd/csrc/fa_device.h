@@ -1,0 +1,121 @@
+// fa_device.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Matrix-core conventions (CDNA 32x32 MFMA, wave64):
+//   D[i][j] = sum_k A[i][k] B[k][j] over one 32 x 32 output block.
+//   A operand: lane l supplies row i = l % 32, B operand: column j = l % 32;
+//   both take their K slice from lane half h = l / 32 in the same slot order,
+//   so any consistent slot -> k assignment contracts correctly.
+//   C/D: lane l holds column j = l % 32; register r holds row
+//   i = 8 * (r / 4) + 4 * h + r % 4.
+//
+// Row permutation. When a 32-row operand is loaded with MFMA row i taking
+// physical row swap_bits23(i), register r of lane half h of the result
+// belongs to physical row 16 * (r / 8) + 8 * h + r % 8. Each lane then owns
+// two runs of 8 consecutive physical rows (registers 0..7 and 8..15), which
+// is exactly the K-slot layout the next product needs: the registers can be
+// rounded to bf16 and fed straight back as a B operand, and the matching A
+// operand is one 16-byte read of 8 consecutive rows from a transposed tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kInf = __builtin_inff();
+
+// Element-type traits: K extent of one MFMA and elements per 16-byte chunk.
+template <typename T> struct Traits;
+template <> struct Traits<bf16> {
+  static constexpr int KC = 16;
+  static constexpr int EPC = 8;
+  typedef bf16x8 Frag;
+};
+template <> struct Traits<float> {
+  static constexpr int KC = 2;
+  static constexpr int EPC = 4;
+  typedef float Frag;
+};
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int swap_bits23(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// Physical row (0..31) of register r in lane half h after a swap_bits23 load.
+__device__ __forceinline__ int perm_row(int r, int h) {
+  return 16 * (r >> 3) + 8 * h + (r & 7);
+}
+
+// Output row (0..31) of register r in lane half h for an unpermuted product.
+__device__ __forceinline__ int c_row(int r, int h) {
+  return 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
+// All-reduce across the two lane halves (lane l and lane l ^ 32).
+__device__ __forceinline__ float half_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  return x + __shfl_xor(x, 32);
+}
+
+// Workgroup index -> logical index. Workgroups are handed to the 8 XCDs of
+// the chip round-robin (w % 8); this bijection gives each XCD a contiguous
+// range of logical indices, so the Q blocks of one head (adjacent logical
+// indices) share that XCD's L2 when they stream the same K/V tiles.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int xcd = w & 7, idx = w >> 3;
+  const int base = total >> 3, rem = total & 7;
+  return xcd * base + (xcd < rem ? xcd : rem) + idx;
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int c) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)s[8 * c + e];
+  return r;
+}
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// 16-byte global load, zero when !ok (the address is not formed then).
+template <typename T>
+__device__ __forceinline__ uint4 ld16(const T* base, int64_t off, bool ok) {
+  return ok ? *reinterpret_cast<const uint4*>(base + off) : zero4();
+}
+
+// Number of valid keys of batch entry b.
+__device__ __forceinline__ int valid_keys(const int32_t* seqlens, int b, int n) {
+  if (!seqlens) return n;
+  int L = seqlens[b];
+  return L < 0 ? 0 : (L > n ? n : L);
+}
+
+// Whether the 128 x 128 block (query row qrow, key col kcol) is present.
+__device__ __forceinline__ bool block_on(const uint8_t* bm, int ld, int qrow, int kcol) {
+  return bm == nullptr || bm[(int64_t)(qrow >> 7) * ld + (kcol >> 7)] != 0;
+}
+
+__device__ __forceinline__ void log_tile(uint32_t* log, int64_t row_word0, int kcol) {
+  const int kb = kcol >> 7;
+  atomicOr(log + row_word0 + (kb >> 5), 1u << (kb & 31));
+}
+
+}  // namespace fa

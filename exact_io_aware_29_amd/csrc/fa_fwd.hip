@@ -1,0 +1,217 @@
+// fa_fwd.hip -- tiled exact-attention forward for gfx950.
+//
+// One workgroup (4 waves, 256 lanes) owns one block of 128 query rows of one
+// (batch, head) -- the Q-outer loop order that FlashAttention-2 introduced
+// (zhaifeiyue.github.io cross-paper synthesis, section 2: outer loop over Q,
+// split-Q work partition between warps). Each wave owns 32 of the rows and
+// streams every visited K/V tile of the head through LDS:
+//
+//   S^T = K_j Q_i^T            bf16 MFMA, fp32 accumulators (32 keys x 32 rows)
+//   mask, row max m~, m_new = max(m, m~), alpha = 2^(m - m_new)
+//   P~ = 2^(s * scale * log2 e - m_new),  l = alpha * l + rowsum(P~)
+//   O^T = alpha * O^T + V_j^T P~^T   bf16 MFMA (P~ rounded to bf16)
+//
+// which is the incremental softmax of the FlashAttention deep-reading report
+// (zako-mio), sections 2.4 and 3.2, in base 2, with the normalisation by l
+// delayed to the end (FlashAttention-2's delayed rescaling). Computing the
+// transposed scores makes every lane own a single query row: the row max is
+// 16 in-register compares plus one exchange with the other lane half, the
+// row sum needs no exchange until the epilogue, and the P~ registers are
+// already in the B-operand layout of the PV product.
+//
+// Tiles with no allowed entry (causal upper triangle, keys past the valid
+// length, absent block-mask blocks) are skipped before they are loaded;
+// element masks are applied only on tiles that straddle a boundary.
+#include "fa_stage.h"
+
+namespace fa {
+
+template <typename T, int D>
+struct FwdCfg {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int BR = 128;                                        // rows per workgroup
+  static constexpr int BC = kBf16 ? (D == 64 ? 128 : 64) : (D == 64 ? 64 : 32);  // keys per tile
+  static constexpr int KC = Traits<T>::KC;
+  static constexpr int EPC = Traits<T>::EPC;
+  static constexpr int NKK = D / KC;     // MFMAs along d per 32 x 32 score block
+  static constexpr int NSUB = BC / 32;   // 32-key sub-tiles per tile
+  static constexpr int NDB = D / 32;     // 32-wide d blocks of O^T
+  static constexpr int KROW = D + EPC;   // K tile pitch (16-byte pad)
+  static constexpr int VROW = BC + EPC;  // transposed V tile pitch (16-byte pad)
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<T, D>;
+  using Frag = typename Traits<T>::Frag;
+  __shared__ __attribute__((aligned(16))) T Ks[C::BC * C::KROW];
+  __shared__ __attribute__((aligned(16))) T Vt[D * C::VROW];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 31, hh = lane >> 5;
+
+  const int nqb = (p.N + C::BR - 1) / C::BR;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head_lin = L / nqb;
+  const int qbi = L - head_lin * nqb;
+  const int qb = p.causal ? nqb - 1 - qbi : qbi;  // causal: longest rows first
+  const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
+  const int q0 = qb * C::BR;
+  const int my_q = q0 + 32 * w + lr;
+
+  const T* Qp = static_cast<const T*>(a.q) + b * a.sq.b + h * a.sq.h;
+  const T* Kp = static_cast<const T*>(a.k) + b * a.sk.b + hk * a.sk.h;
+  const T* Vp = static_cast<const T*>(a.v) + b * a.sv.b + hk * a.sv.h;
+
+  const int kvalid = valid_keys(p.seqlens, b, p.N);
+  const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
+  const int ntiles = (kend + C::BC - 1) / C::BC;
+
+  // This lane's query row as the B operand of S^T = K Q^T.
+  Frag qf[C::NKK];
+  {
+    const bool ok = my_q < p.N;
+    const T* qrow = Qp + (int64_t)(ok ? my_q : 0) * a.sq.n + hh * (C::KC / 2);
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = frag_g(qrow + kk * C::KC, ok);
+  }
+
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+  float m_run = -kInf;  // running max of raw scores
+  float l_run = 0.f;    // this lane half's share of the running exp-sum
+  const float sl2 = p.scale_l2;
+  const int64_t log_row =
+      a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int key0 = kt * C::BC;
+    if (!block_on(p.bm, p.bm_ld, q0, key0)) continue;  // uniform per workgroup
+    __syncthreads();
+    stage_rows<T, D, C::BC, C::KROW>(Kp, a.sk.n, key0, p.N, Ks, tid);
+    stage_cols<T, D, C::BC, C::VROW>(Vp, a.sv.n, key0, p.N, Vt, tid);
+    __syncthreads();
+    if (a.log && tid == 0) log_tile(a.log, log_row, key0);
+
+    // S^T for this wave's 32 rows against the tile's keys.
+    f32x16 s[C::NSUB];
+#pragma unroll
+    for (int t = 0; t < C::NSUB; ++t) {
+      s[t] = f32x16{};
+      const T* krow = Ks + (32 * t + swap_bits23(lr)) * C::KROW + hh * (C::KC / 2);
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) s[t] = mfma(frag<T>(krow + kk * C::KC), qf[kk], s[t]);
+    }
+
+    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+    if (need_mask) {
+#pragma unroll
+      for (int t = 0; t < C::NSUB; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * t + perm_row(r, hh);
+          if ((p.causal && key > my_q) || key >= kvalid) s[t][r] = -kInf;
+        }
+    }
+
+    float mx = -kInf;
+#pragma unroll
+    for (int t = 0; t < C::NSUB; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    mx = half_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_ref = (m_new == -kInf) ? 0.f : m_new * sl2;
+    const float alpha = __builtin_amdgcn_exp2f(m_run * sl2 - m_ref);
+    m_run = m_new;
+
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < C::NSUB; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, -m_ref));
+        s[t][r] = e;
+        psum += e;
+      }
+    l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+
+    // O^T += V^T P~^T: the P~ registers are the B operand directly.
+#pragma unroll
+    for (int t = 0; t < C::NSUB; ++t) {
+      if constexpr (C::kBf16) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 pf = pack8(s[t], c);
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const T* vp = Vt + (32 * db + lr) * C::VROW + 32 * t + 16 * c + 8 * hh;
+            acc[db] = mfma(frag<T>(vp), pf, acc[db]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const float vf = Vt[(32 * db + lr) * C::VROW + 32 * t + perm_row(r, hh)];
+            acc[db] = mfma(vf, s[t][r], acc[db]);
+          }
+        }
+      }
+    }
+  }
+
+  // Epilogue: O = O~ / l, LSE = m * scale + ln l (natural log).
+  const float l_tot = half_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (my_q < p.N) {
+    char* obase = static_cast<char*>(a.o);
+    const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * hh;
+        const float v0 = acc[db][4 * g] * inv, v1 = acc[db][4 * g + 1] * inv;
+        const float v2 = acc[db][4 * g + 2] * inv, v3 = acc[db][4 * g + 3] * inv;
+        if (a.o_fp32) {
+          *reinterpret_cast<float4*>(obase + (orow + d0) * 4) = make_float4(v0, v1, v2, v3);
+        } else {
+          bf16x4 pk;
+          pk[0] = (bf16)v0;
+          pk[1] = (bf16)v1;
+          pk[2] = (bf16)v2;
+          pk[3] = (bf16)v3;
+          *reinterpret_cast<bf16x4*>(obase + (orow + d0) * 2) = pk;
+        }
+      }
+    if (hh == 0) {
+      const float lse = l_tot > 0.f ? (m_run * sl2 + __log2f(l_tot)) * kLn2 : -kInf;
+      a.lse[((int64_t)b * p.Hq + h) * p.N + my_q] = lse;
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
+  const int64_t nqb = (a.p.N + 127) / 128;
+  const int64_t grid = nqb * a.p.Hq * a.p.B;
+  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, hipStream_t s) {
+  if (dtype == 0) {
+    return head_dim == 64 ? launch_fwd_t<bf16, 64>(a, s) : launch_fwd_t<bf16, 128>(a, s);
+  }
+  return head_dim == 64 ? launch_fwd_t<float, 64>(a, s) : launch_fwd_t<float, 128>(a, s);
+}
+
+}  // namespace fa

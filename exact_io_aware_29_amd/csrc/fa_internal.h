@@ -1,0 +1,62 @@
+// fa_internal.h -- argument blocks passed from the C ABI layer to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct Strides {
+  int64_t b, h, n;
+};
+
+// Shape and mask of one call, already validated on the host.
+struct Problem {
+  int B, Hq, Hkv, N, G;
+  float scale;      // softmax scale (> 0)
+  float scale_l2;   // scale * log2(e): scores enter exp2 in this unit
+  int causal;
+  const int32_t* seqlens;  // device [B] or null
+  const uint8_t* bm;       // device block mask or null
+  int bm_ld;
+  int nlb;   // ceil(N / 128): 128-blocks per sequence
+  int logw;  // uint32 words per tile-log row: ceil(nlb / 32)
+};
+
+struct FwdArgs {
+  Problem p;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  Strides sq, sk, sv, so;
+  float* lse;
+  uint32_t* log;
+  int o_fp32;
+};
+
+struct BwdArgs {
+  Problem p;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  const float* lse;
+  float* dvec;  // workspace: D = rowsum(dO * O), fp32 [B][Hq][N]
+  void* dq;
+  void* dk;
+  void* dv;
+  uint32_t* log_kv;  // tiles visited by the dK/dV kernel (or null)
+  uint32_t* log_q;   // tiles visited by the dQ kernel (or null)
+  int o_fp32;
+};
+
+// Launchers (defined next to their kernels). dtype: 0 bf16, 1 fp32.
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,193 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * The library computes exact scaled-dot-product attention,
+ *     O = softmax(Q K^T * scale + mask) V,
+ * the way the FlashAttention method computes it: Q is split into row blocks,
+ * K/V are streamed through on-chip memory tile by tile, and a running row
+ * maximum m and scaled exponential sum l (the incremental softmax of the
+ * FlashAttention deep-reading report, zako-mio, sections 2.4 and 3.2) keep
+ * the result exact without the N x N score or probability matrix ever being
+ * written to device memory. The backward pass is the recomputation backward
+ * of the report's sections 2.5 and 3.3: the forward saves only O and one
+ * statistic per row (here the natural log-sum-exp LSE = m + ln l), and the
+ * backward rebuilds P tile by tile from Q, K and LSE.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are addressed as base + b*stride.batch + h*stride.head
+ * + i*stride.row + t, with element (not byte) strides and unit stride along
+ * the head dimension t. Q, O, dO and dQ have heads_q heads; K, V, dK and dV
+ * have heads_kv heads. Query head h reads key/value head h / G with
+ * G = heads_q / heads_kv (grouped-query attention, as in the bowenzhou.top
+ * tutorial's remark that K/V heads may be shared).
+ *
+ * Masks, all combined with AND (a disallowed score counts as -infinity):
+ *   causal     key j is allowed for query i iff j <= i (top-left aligned);
+ *   seqlens_k  key j is allowed iff j < seqlens_k[b] (key padding); query
+ *              rows past the valid length are still computed;
+ *   block_mask key j is allowed for query i iff
+ *              block_mask[(i/128)*block_mask_ld + j/128] != 0; this is the
+ *              block-sparse variant of the report's sections 2.6 and 3.5 at a
+ *              fixed 128 x 128 granularity, shared by all batches and heads.
+ * A 128 x 128 tile with no allowed entry is skipped whole: never loaded and
+ * never computed. A query row with no allowed key gets O = 0 and
+ * LSE = -infinity, and contributes nothing to the gradients.
+ *
+ * Ownership: the caller allocates and owns every buffer (inputs, outputs,
+ * workspace, tile logs). The library never allocates device memory, frees
+ * nothing and keeps no pointer after the call returns. Every call only
+ * enqueues work on `stream` (a hipStream_t; NULL = the default stream) and
+ * returns; device-side faults surface at the caller's next synchronisation.
+ * Inputs are read-only; outputs are overwritten and must not alias inputs.
+ *
+ * Errors: every entry point validates its arguments on the host before any
+ * HIP call and returns a negative fa_status on failure without touching the
+ * GPU. FA_ERR_HIP means a HIP launch failed; fa_last_error_detail() then
+ * holds the HIP error text. No entry point aborts or throws.
+ *
+ * The library keeps no global mutable state apart from the per-thread error
+ * detail, so calls on different streams may run concurrently.
+ */
+#ifndef EXACT_IO_AWARE_FA_H
+#define EXACT_IO_AWARE_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,     /* a size is <= 0, or too large to index */
+  FA_ERR_DTYPE = -3,     /* unsupported dtype combination */
+  FA_ERR_HEADDIM = -4,   /* head_dim is not 64 or 128 */
+  FA_ERR_GQA = -5,       /* heads_q is not a multiple of heads_kv */
+  FA_ERR_STRIDE = -6,    /* a stride is negative or not a multiple of 16 bytes */
+  FA_ERR_ALIGN = -7,     /* a base pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = -8, /* workspace missing or smaller than required */
+  FA_ERR_HIP = -9,       /* a HIP call failed (see fa_last_error_detail) */
+  FA_ERR_MASK = -10,     /* block_mask_ld smaller than ceil(seqlen / 128) */
+  FA_ERR_SCALE = -11     /* scale is not finite and positive */
+};
+
+/* Element types. */
+enum fa_dtype {
+  FA_BF16 = 0, /* bfloat16 storage; all arithmetic accumulates in fp32 */
+  FA_FP32 = 1  /* float32 storage and fp32 matrix-core arithmetic */
+};
+
+/* Granularity of block masks and of tile logs (rows and columns). */
+#define FA_MASK_BLOCK 128
+
+/* Element strides of a [batch][head][row][head_dim] tensor. */
+typedef struct fa_strides {
+  int64_t batch;
+  int64_t head;
+  int64_t row;
+} fa_strides;
+
+/* Problem description shared by the forward and backward entry points. */
+typedef struct fa_params {
+  int32_t dtype;    /* fa_dtype of Q, K, V (and of dO, dQ, dK, dV) */
+  int32_t o_dtype;  /* fa_dtype of O: equal to dtype, or FA_FP32 with bf16 */
+  int32_t batch;    /* B >= 1 */
+  int32_t heads_q;  /* query heads >= 1 */
+  int32_t heads_kv; /* key/value heads >= 1, divides heads_q */
+  int32_t seqlen;   /* N >= 1: query and key length */
+  int32_t head_dim; /* d: 64 or 128 */
+  float scale;      /* softmax scale, usually 1/sqrt(d) */
+  int32_t causal;   /* nonzero: causal mask */
+  const int32_t* seqlens_k;  /* device [batch] valid key counts, or NULL;
+                                values are clamped to [0, seqlen] */
+  const uint8_t* block_mask; /* device [ceil(N/128)][block_mask_ld], or NULL */
+  int32_t block_mask_ld;     /* row pitch of block_mask in bytes */
+} fa_params;
+
+/*
+ * fa_fwd -- tiled forward pass (the report's section 3.2, with the loop
+ * order of FlashAttention-2 described in the zhaifeiyue.github.io
+ * cross-paper synthesis, section 2: one workgroup per Q block, K/V streamed).
+ *
+ *   q, k, v   device inputs of dtype p->dtype with strides sq, sk, sv
+ *   o         device output [B][heads_q][N][d] of dtype p->o_dtype (strides so)
+ *   lse       device output, contiguous float32 [B][heads_q][N]: natural
+ *             log-sum-exp of each row's scaled, masked scores (-inf if empty)
+ *   tile_log  NULL, or a caller-zeroed device array of fa_tile_log_words(p)
+ *             uint32 words; bit (kb % 32) of word
+ *             ((b*heads_q + h)*ceil(N/128) + qb)*ceil(ceil(N/128)/32) + kb/32
+ *             is set iff the kernel loaded and computed any part of the
+ *             128 x 128 tile (qb, kb) of batch b, head h
+ *   stream    hipStream_t to enqueue on
+ * Supports dtype FA_BF16 (o_dtype FA_BF16 or FA_FP32) and FA_FP32.
+ */
+int fa_fwd(const fa_params* p,
+           const void* q, fa_strides sq,
+           const void* k, fa_strides sk,
+           const void* v, fa_strides sv,
+           void* o, fa_strides so,
+           float* lse,
+           uint32_t* tile_log,
+           void* stream);
+
+/* Number of uint32 words of one tile log (fa_fwd); fa_bwd takes twice this. */
+size_t fa_tile_log_words(const fa_params* p);
+
+/* Bytes of device workspace fa_bwd needs (the row vector D, fp32 [B][Hq][N]). */
+size_t fa_bwd_workspace_size(const fa_params* p);
+
+/*
+ * fa_bwd -- recomputation backward (the report's sections 2.5 and 3.3; the
+ * tutorial's backward paragraph). Three kernels run in order on `stream`:
+ *   1. D_i = sum_t dO[i][t] * O[i][t] into the workspace (fp32);
+ *   2. per block of 128 keys of one key/value head: for every query head of
+ *      its group and every visited query tile, rebuild
+ *      P = exp(scale * q.k - LSE), dP = dO V^T, dS = P * (dP - D) and
+ *      accumulate dV += P^T dO and dK += scale * dS^T Q (fp32 registers);
+ *   3. per block of 128 query rows: rebuild P and dS the same way and
+ *      accumulate dQ += scale * dS K.
+ *
+ *   q, k, v, o, dout  device inputs (o of dtype p->o_dtype, the others of
+ *                     p->dtype) with their strides
+ *   lse               the forward's log-sum-exp, float32 [B][heads_q][N]
+ *   dq, dk, dv        device outputs of dtype p->dtype (overwritten)
+ *   workspace         device buffer of >= fa_bwd_workspace_size(p) bytes,
+ *                     16-byte aligned; its contents on entry are ignored
+ *   tile_log          NULL, or caller-zeroed 2 * fa_tile_log_words(p) words:
+ *                     first the tiles visited by kernel 2, then by kernel 3
+ *                     (same bit layout as fa_fwd)
+ *   stage_events      NULL, or 4 hipEvent_t recorded on `stream` before
+ *                     kernel 1, before kernel 2, before kernel 3 and after
+ *                     kernel 3 (for per-kernel timing)
+ * Supports dtype FA_BF16 only (FA_ERR_DTYPE otherwise).
+ */
+int fa_bwd(const fa_params* p,
+           const void* q, fa_strides sq,
+           const void* k, fa_strides sk,
+           const void* v, fa_strides sv,
+           const void* o, fa_strides so,
+           const void* dout, fa_strides sdo,
+           const float* lse,
+           void* dq, fa_strides sdq,
+           void* dk, fa_strides sdk,
+           void* dv, fa_strides sdv,
+           void* workspace, size_t workspace_bytes,
+           uint32_t* tile_log,
+           void* const* stage_events,
+           void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa_strerror(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* fa_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_IO_AWARE_FA_H */
