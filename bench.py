@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one forward (fa_fwd) and one backward (fa_bwd: D preprocess,
+dK/dV kernel, dQ kernel) over one batch of synthetic inputs that are already
+resident in HBM. The default workload is GPT-2-medium-shaped attention:
+batch 64, 16 heads, N = 1024, d = 64, bf16, non-causal (the FlashAttention
+paper's forward+backward micro-benchmark shape).
+
+Prints one JSON line with whole-job throughput (algorithmic fwd+bwd TFLOP/s),
+per-kernel HIP-event timings, the dominant kernel's roofline position, and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd & fwd+bwd TFLOP/s + % of bf16 MFMA peak, B64 H16 N1024 d64"
+KERNEL_SOURCES = {
+    "fwd": ["fa_fwd.hip", "fa_stage.h", "fa_device.h"],
+    "bwd_dkdv": ["fa_bwd.hip", "fa_stage.h", "fa_device.h"],
+    "bwd_dq": ["fa_bwd.hip", "fa_stage.h", "fa_device.h"],
+    "bwd_pre": ["fa_bwd.hip"],
+}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="workload id (2 = the headline B64 H16 N1024 d64 shape)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_io_aware_29_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: int):
+    """HBM bytes per launch measured by rocprofv3 counters, if the summary in
+    profiles/ was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_w{workload}.md")
+    if not os.path.exists(path):
+        return None
+    pat = re.compile(r"^traffic\s+(\S+)\s+bytes_per_launch=(\d+)\s+src=(\w+)", re.M)
+    with open(path) as fh:
+        for name, nbytes, src in pat.findall(fh.read()):
+            if name == kernel and src == source_hash(kernel):
+                return int(nbytes)
+    return None
+
+
+def cpu_baseline(inp, pairs_per_head, budget_s):
+    """Time the fp64 oracle's forward + backward head by head until the time
+    budget is spent; report algorithmic TFLOP/s over the heads done."""
+    import numpy as np
+    import oracle
+    from oracle.attention import mask_for
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    w = inp.workload
+    G = w.heads_q // w.heads_kv
+    done, flop = 0, 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        m = mask_for(b, causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask)
+        for h in range(w.heads_q):
+            q = inp.as_f64("q", (b, h))
+            k = inp.as_f64("k", (b, h // G))
+            v = inp.as_f64("v", (b, h // G))
+            oracle.head_forward(q, k, v, inp.scale, m)
+            if w.backward:
+                oracle.head_backward(q, k, v, inp.as_f64("do", (b, h)), inp.scale, m)
+            done += 1
+            flop += (14 if w.backward else 4) * w.head_dim * pairs_per_head[b]
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": round(flop / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"fp64 oracle {'fwd+bwd' if w.backward else 'fwd'} of the first {done} (batch, head) pairs of "
+                  f"{w.batch * w.heads_q}, {el:.1f} s; same algorithmic flop count",
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards over "
+              "(batch, head) with no communication, so one GPU's figure is the per-GPU rate.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_io_aware_29_amd as fa
+    from exact_io_aware_29_amd import accounting as acc
+    from synth import WORKLOADS, draw
+
+    w = WORKLOADS[args.workload]
+    inp = draw(w, args.workload)
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = t(inp.q), t(inp.k), t(inp.v)
+    do = t(inp.do) if w.backward else None
+    sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).to(dev)
+    bm = None if inp.block_mask is None else torch.from_numpy(inp.block_mask).to(dev)
+    kw = dict(scale=inp.scale, causal=w.causal, seqlens_k=sl, block_mask=bm)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    if w.backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        p = fa.make_params(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
+                           seqlen=w.seqlen, head_dim=w.head_dim)
+        ws = torch.empty(fa.fa_bwd_workspace_size(p) // 4 + 4, dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_fwd(q, k, v, out=o, lse=lse, **kw)
+        if ev is not None:
+            ev[1].record()
+        if w.backward:
+            fa.fa_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws,
+                      stage_events=None if ev is None else ev[2:6], **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record()  # create the events outside the timed region
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    def avg_ms(a, b):
+        return float(np.mean([events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)]))
+
+    kern_ms = {"fwd": avg_ms(0, 1)}
+    if w.backward:
+        kern_ms.update(bwd_pre=avg_ms(2, 3), bwd_dkdv=avg_ms(3, 4), bwd_dq=avg_ms(4, 5))
+
+    per_b = [int(acc.allowed_pairs_per_row(
+        w.seqlen, causal=w.causal, seqlen_k=None if inp.seqlens is None else int(inp.seqlens[b]),
+        block_mask=inp.block_mask).sum()) for b in range(w.batch)]
+    pairs = sum(per_b) * w.heads_q
+    fl = acc.flops(pairs, w.head_dim)
+    ms_step = wall / args.steps * 1e3
+    step_flop = fl["fwd_bwd"] if w.backward else fl["fwd"]
+    value = step_flop / (ms_step * 1e-3) / 1e12
+    peak = acc.MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else acc.MFMA_FP32_PEAK_TFLOPS
+    eb = 2 if w.dtype == "bf16" else 4
+
+    kernels = {}
+    for name, ms in kern_ms.items():
+        if name == "bwd_pre":
+            nbytes = acc.bwd_pre_bytes(w.batch, w.heads_q, w.seqlen, w.head_dim, eb, eb)
+            ach = nbytes / (ms * 1e-3) / 1e9
+            kernels[name] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1),
+                             "peak": acc.HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(ach / acc.HBM_PEAK_GBS, 4)}
+        else:
+            ach = fl[name] / (ms * 1e-3) / 1e12
+            kernels[name] = {"ms": round(ms, 4), "bound": "mfma", "achieved": round(ach, 1),
+                             "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+    dom = max(kern_ms, key=kern_ms.get)
+    dk_ = kernels[dom]
+    roofline = {"kernel": dom, "bound": dk_["bound"], "achieved": dk_["achieved"],
+                "peak": dk_["peak"], "unit": dk_["unit"], "frac": dk_["frac"],
+                "traffic": recorded_traffic(dom, args.workload)}
+
+    fwd_tf = fl["fwd"] / (kern_ms["fwd"] * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, rounded to bf16)",
+        "config": {"workload": w.describe(), "batch": w.batch, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "seqlen": w.seqlen, "head_dim": w.head_dim,
+                   "causal": w.causal, "pass": "fwd+bwd" if w.backward else "fwd"},
+        "pct_of_peak_fwd_bwd": round(100 * value / peak, 2),
+        "fwd_tflops": round(fwd_tf, 2),
+        "pct_of_peak_fwd": round(100 * fwd_tf / peak, 2),
+        "algorithmic_flop": {"fwd": fl["fwd"], "fwd_bwd": fl["fwd_bwd"], "pairs": pairs},
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, per_b, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
