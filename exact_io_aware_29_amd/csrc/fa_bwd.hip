@@ -75,24 +75,24 @@ __device__ __forceinline__ float lse2_of(float lse) {
 
 template <int D>
 struct DkdvCfg {
-  static constexpr int BK = 128;       // keys per workgroup
-  static constexpr int BQ = 4096 / D;  // query rows staged per step
+  static constexpr int BK = 128;       // keys per workgroup (4 waves x 32)
+  static constexpr int BQ = 8192 / D;  // query rows staged per step
   static constexpr int NQS = BQ / 32;
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int QROW = D + 8;   // row-major Q / dO pitch
-  static constexpr int TROW = BQ + 8;  // transposed Q / dO pitch
+  using G = TileGeom<D, BQ>;
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[C::BQ * C::QROW];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[C::BQ * C::QROW];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[D * C::TROW];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[D * C::TROW];
-  __shared__ float lse_s[C::BQ];
-  __shared__ float dvec_s[C::BQ];
+  using G = typename C::G;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[C::BQ * G::RPITCH];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[C::BQ * G::RPITCH];
+  __shared__ __attribute__((aligned(16))) bf16 Qt[D * G::TPITCH];
+  __shared__ __attribute__((aligned(16))) bf16 dOt[D * G::TPITCH];
+  __shared__ __attribute__((aligned(16))) float lse_s[C::BQ];
+  __shared__ __attribute__((aligned(16))) float dvec_s[C::BQ];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -130,65 +130,108 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int kvalid = valid_keys(p.seqlens, b, p.N);
   if (k0 < kvalid) {  // else every key of the block is masked: dK = dV = 0
-    const int qstart = p.causal ? k0 : 0;  // rows above the diagonal see none of these keys
-    const int nqblk = (p.N + C::BQ - 1) / C::BQ;
-    for (int gi = 0; gi < p.G; ++gi) {
-      const int h = hk * p.G + gi;
-      const bf16* Qp = static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h;
-      const bf16* dOp = static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h;
-      const float* lse_row = a.lse + ((int64_t)b * p.Hq + h) * p.N;
-      const float* dvec_row = a.dvec + ((int64_t)b * p.Hq + h) * p.N;
-      for (int qblk = qstart / C::BQ; qblk < nqblk; ++qblk) {
-        const int q0b = qblk * C::BQ;
-        if (!block_on(p.bm, p.bm_ld, q0b, k0)) continue;  // uniform per workgroup
-        __syncthreads();
-        stage_rows<bf16, D, C::BQ, C::QROW>(Qp, a.sq.n, q0b, p.N, Qs, tid);
-        stage_cols<bf16, D, C::BQ, C::TROW>(Qp, a.sq.n, q0b, p.N, Qt, tid);
-        stage_rows<bf16, D, C::BQ, C::QROW>(dOp, a.sdo.n, q0b, p.N, dOs, tid);
-        stage_cols<bf16, D, C::BQ, C::TROW>(dOp, a.sdo.n, q0b, p.N, dOt, tid);
-        if (tid < C::BQ) {
-          const int qi = q0b + tid;
-          lse_s[tid] = qi < p.N ? lse2_of(lse_row[qi]) : kInf;
-          dvec_s[tid] = qi < p.N ? dvec_row[qi] : 0.f;
-        }
-        __syncthreads();
-        if (a.log_kv && tid == 0)
-          log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
+    // Steps run over (query head of the group) x (query block); rows above
+    // the diagonal see none of these keys under the causal mask.
+    const int qfirst = p.causal ? k0 / C::BQ : 0;
+    const int nq = (p.N + C::BQ - 1) / C::BQ - qfirst;
+    const int nsteps = p.G * nq;
+    auto next_step = [&](int st) {
+      while (st < nsteps && !block_on(p.bm, p.bm_ld, (qfirst + st % nq) * C::BQ, k0)) ++st;
+      return st;
+    };
+    const int arow = swap_bits23(lr) * G::RPITCH + 8 * hh;
+    int trow[C::NDB], tsw[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      trow[db] = (32 * db + lr) * G::TPITCH;
+      tsw[db] = (4 * db + (lr >> 3)) & 7;
+    }
 
-        const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid);
+    ColRegs<D, C::BQ> qreg, doreg;
+    float lse_r = 0.f, dvec_r = 0.f;
+    auto fetch = [&](int st) {
+      const int h = hk * p.G + st / nq;
+      const int q0b = (qfirst + st % nq) * C::BQ;
+      load_cols<D, C::BQ>(qreg, static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h, a.sq.n,
+                          q0b, p.N, tid);
+      load_cols<D, C::BQ>(doreg, static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
+                          a.sdo.n, q0b, p.N, tid);
+      if (tid < C::BQ) {
+        const int qi = q0b + tid;
+        const int64_t off = ((int64_t)b * p.Hq + h) * p.N + qi;
+        lse_r = qi < p.N ? lse2_of(a.lse[off]) : kInf;
+        dvec_r = qi < p.N ? a.dvec[off] : 0.f;
+      }
+    };
+    auto stage = [&]() {
+      store_rows_t<D, C::BQ>(qreg, Qs, tid);
+      store_cols<D, C::BQ>(qreg, Qt, tid);
+      store_rows_t<D, C::BQ>(doreg, dOs, tid);
+      store_cols<D, C::BQ>(doreg, dOt, tid);
+      if (tid < C::BQ) {
+        lse_s[tid] = lse_r;
+        dvec_s[tid] = dvec_r;
+      }
+    };
+
+    int st = next_step(0);
+    if (st < nsteps) {
+      fetch(st);
+      stage();
+      __syncthreads();
+    }
+    while (st < nsteps) {
+      const int h = hk * p.G + st / nq;
+      const int q0b = (qfirst + st % nq) * C::BQ;
+      const int nx = next_step(st + 1);
+      if (nx < nsteps) fetch(nx);  // in flight during this step
+      if (a.log_kv && tid == 0)
+        log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
+      const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid);
+
 #pragma unroll
-        for (int u = 0; u < C::NQS; ++u) {
-          f32x16 s = f32x16{}, dp = f32x16{};
-          const int arow = (32 * u + swap_bits23(lr)) * C::QROW + 8 * hh;
+      for (int u = 0; u < C::NQS; ++u) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const int ao = 32 * u * G::RPITCH + arow;
 #pragma unroll
-          for (int kk = 0; kk < C::NKK; ++kk) {
-            s = mfma(frag<bf16>(Qs + arow + 16 * kk), kf[kk], s);
-            dp = mfma(frag<bf16>(dOs + arow + 16 * kk), vf[kk], dp);
+        for (int kk = 0; kk < C::NKK; ++kk) {
+          s = mfma(frag<bf16>(Qs + ao + 16 * kk), kf[kk], s);
+          dp = mfma(frag<bf16>(dOs + ao + 16 * kk), vf[kk], dp);
+        }
+        // Register r holds query row 32u + perm_row(r, hh) of this step.
+        const f32x4* l4 = reinterpret_cast<const f32x4*>(lse_s + 32 * u + 8 * hh);
+        const f32x4* d4 = reinterpret_cast<const f32x4*>(dvec_s + 32 * u + 8 * hh);
+        f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
+        f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[r >> 2][r & 3]));
+          if (need_mask) {
+            const int qi = q0b + 32 * u + perm_row(r, hh);
+            if ((p.causal && my_k > qi) || my_k >= kvalid) pv = 0.f;
           }
+          s[r] = pv;
+          dp[r] = pv * (dp[r] - dv4[r >> 2][r & 3]);
+        }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ql = 32 * u + perm_row(r, hh);
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse_s[ql]));
-            if (need_mask) {
-              const int qi = q0b + ql;
-              if ((p.causal && my_k > qi) || my_k >= kvalid) pv = 0.f;
-            }
-            s[r] = pv;
-            dp[r] = pv * (dp[r] - dvec_s[ql]);
-          }
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 pf = pack8(s, c);
+          const bf16x8 dsf = pack8(dp, c);
+          const int kc = 4 * u + 2 * c + hh;
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const bf16x8 pf = pack8(s, c);
-            const bf16x8 dsf = pack8(dp, c);
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-              const int trow = (32 * db + lr) * C::TROW + 32 * u + 16 * c + 8 * hh;
-              dvt[db] = mfma(frag<bf16>(dOt + trow), pf, dvt[db]);
-              dkt[db] = mfma(frag<bf16>(Qt + trow), dsf, dkt[db]);
-            }
+          for (int db = 0; db < C::NDB; ++db) {
+            const int to = trow[db] + 8 * (kc ^ tsw[db]);
+            dvt[db] = mfma(frag<bf16>(dOt + to), pf, dvt[db]);
+            dkt[db] = mfma(frag<bf16>(Qt + to), dsf, dkt[db]);
           }
         }
       }
+      if (nx < nsteps) {
+        __syncthreads();
+        stage();
+        __syncthreads();
+      }
+      st = nx;
     }
   }
 
@@ -217,20 +260,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 template <int D>
 struct DqCfg {
   static constexpr int BR = 128;       // query rows per workgroup
-  static constexpr int BC = 8192 / D;  // keys per tile (64 or 128)
+  static constexpr int BC = 8192 / D;  // keys per tile (128 or 64)
   static constexpr int NSUB = BC / 32;
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int KROW = D + 8;   // row-major K / V pitch
-  static constexpr int TROW = BC + 8;  // transposed K pitch
+  using G = TileGeom<D, BC>;
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[C::BC * C::KROW];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[C::BC * C::KROW];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[D * C::TROW];
+  using G = typename C::G;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[C::BC * G::RPITCH];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[C::BC * G::RPITCH];
+  __shared__ __attribute__((aligned(16))) bf16 Kt[D * G::TPITCH];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -273,26 +316,48 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int ntiles = (kend + C::BC - 1) / C::BC;
   const int64_t log_row =
       a.log_q ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+  auto next_visit = [&](int kt) {
+    while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
+    return kt;
+  };
+  const int arow = swap_bits23(lr) * G::RPITCH + 8 * hh;
+  int trow[C::NDB], tsw[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    trow[db] = (32 * db + lr) * G::TPITCH;
+    tsw[db] = (4 * db + (lr >> 3)) & 7;
+  }
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  ColRegs<D, C::BC> kreg, vreg;
+  auto stage = [&]() {
+    store_rows_t<D, C::BC>(kreg, Ks, tid);
+    store_cols<D, C::BC>(kreg, Kt, tid);
+    store_rows_t<D, C::BC>(vreg, Vs, tid);
+  };
+  int kt = next_visit(0);
+  if (kt < ntiles) {
+    load_cols<D, C::BC>(kreg, Kp, a.sk.n, kt * C::BC, p.N, tid);
+    load_cols<D, C::BC>(vreg, Vp, a.sv.n, kt * C::BC, p.N, tid);
+    stage();
+    __syncthreads();
+  }
+  while (kt < ntiles) {
     const int key0 = kt * C::BC;
-    if (!block_on(p.bm, p.bm_ld, q0, key0)) continue;
-    __syncthreads();
-    stage_rows<bf16, D, C::BC, C::KROW>(Kp, a.sk.n, key0, p.N, Ks, tid);
-    stage_rows<bf16, D, C::BC, C::KROW>(Vp, a.sv.n, key0, p.N, Vs, tid);
-    stage_cols<bf16, D, C::BC, C::TROW>(Kp, a.sk.n, key0, p.N, Kt, tid);
-    __syncthreads();
+    const int nxt = next_visit(kt + 1);
+    if (nxt < ntiles) {
+      load_cols<D, C::BC>(kreg, Kp, a.sk.n, nxt * C::BC, p.N, tid);
+      load_cols<D, C::BC>(vreg, Vp, a.sv.n, nxt * C::BC, p.N, tid);
+    }
     if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
-
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
       f32x16 st = f32x16{}, dpt = f32x16{};
-      const int arow = (32 * t + swap_bits23(lr)) * C::KROW + 8 * hh;
+      const int ao = 32 * t * G::RPITCH + arow;
 #pragma unroll
       for (int kk = 0; kk < C::NKK; ++kk) {
-        st = mfma(frag<bf16>(Ks + arow + 16 * kk), qf[kk], st);
-        dpt = mfma(frag<bf16>(Vs + arow + 16 * kk), dof[kk], dpt);
+        st = mfma(frag<bf16>(Ks + ao + 16 * kk), qf[kk], st);
+        dpt = mfma(frag<bf16>(Vs + ao + 16 * kk), dof[kk], dpt);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -306,12 +371,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 dsf = pack8(dpt, c);
+        const int kc = 4 * t + 2 * c + hh;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
-          acc[db] = mfma(frag<bf16>(Kt + (32 * db + lr) * C::TROW + 32 * t + 16 * c + 8 * hh), dsf,
-                         acc[db]);
+          acc[db] = mfma(frag<bf16>(Kt + trow[db] + 8 * (kc ^ tsw[db])), dsf, acc[db]);
       }
     }
+    if (nxt < ntiles) {
+      __syncthreads();
+      stage();
+      __syncthreads();
+    }
+    kt = nxt;
   }
 
   if (qok) {

@@ -69,12 +69,22 @@ __device__ __forceinline__ int c_row(int r, int h) {
 }
 
 // All-reduce across the two lane halves (lane l and lane l ^ 32).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; applied to (x, x) it leaves x[l % 32] in one
+// result and x[l % 32 + 32] in the other, in every lane.
 __device__ __forceinline__ float half_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_sum(float x) {
-  return x + __shfl_xor(x, 32);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// True in every lane if `pred` holds in any active lane of the wave.
+__device__ __forceinline__ bool wave_any(bool pred) { return __any(pred); }
 
 // Workgroup index -> logical index. Workgroups are handed to the 8 XCDs of
 // the chip round-robin (w % 8); this bijection gives each XCD a contiguous

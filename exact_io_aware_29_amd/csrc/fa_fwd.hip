@@ -199,6 +199,184 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ bf16
+
+template <int D>
+struct FwdB {
+  static constexpr int BR = 128;                  // rows per workgroup (4 waves x 32)
+  static constexpr int BC = D == 64 ? 128 : 64;   // keys per tile
+  static constexpr int NKK = D / 16;
+  static constexpr int NSUB = BC / 32;
+  static constexpr int NDB = D / 32;
+  using G = TileGeom<D, BC>;
+  // Running maxima are allowed to lag the true row maximum by up to this
+  // much (log2 units): P~ then stays below 2^8, which bf16 and the fp32 sums
+  // hold exactly as well as values below 1, and the O rescale (one multiply
+  // per accumulator) is only paid when a row's maximum really grows.
+  static constexpr float kLag = 8.f;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
+  using C = FwdB<D>;
+  using G = typename C::G;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[C::BC * G::RPITCH];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[D * G::TPITCH];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 31, hh = lane >> 5;
+
+  const int nqb = (p.N + C::BR - 1) / C::BR;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head_lin = L / nqb;
+  const int qbi = L - head_lin * nqb;
+  const int qb = p.causal ? nqb - 1 - qbi : qbi;  // causal: longest rows first
+  const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
+  const int q0 = qb * C::BR;
+  const int my_q = q0 + 32 * w + lr;
+
+  const bf16* Kp = static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h;
+  const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
+
+  const int kvalid = valid_keys(p.seqlens, b, p.N);
+  const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
+  const int ntiles = (kend + C::BC - 1) / C::BC;
+
+  bf16x8 qf[C::NKK];
+  {
+    const bool ok = my_q < p.N;
+    const bf16* qrow = static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h +
+                       (int64_t)(ok ? my_q : 0) * a.sq.n + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = frag_g(qrow + 16 * kk, ok);
+  }
+
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+  float m_ref = -kInf;  // exponent reference of this lane's row (log2 units)
+  float l_run = 0.f;    // this lane half's share of the row's exp-sum
+  const float sl2 = p.scale_l2;
+  const int64_t log_row =
+      a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+
+  const int krow_off = swap_bits23(lr) * G::RPITCH + 8 * hh;
+  int vrow_off[C::NDB], vsw[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    vrow_off[db] = (32 * db + lr) * G::TPITCH;
+    vsw[db] = (4 * db + (lr >> 3)) & 7;
+  }
+
+  RowRegs<D, C::BC> kreg;
+  ColRegs<D, C::BC> vreg;
+  auto next_visit = [&](int kt) {
+    while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
+    return kt;
+  };
+
+  int kt = next_visit(0);
+  if (kt < ntiles) {
+    load_rows<D, C::BC>(kreg, Kp, a.sk.n, kt * C::BC, p.N, tid);
+    load_cols<D, C::BC>(vreg, Vp, a.sv.n, kt * C::BC, p.N, tid);
+    store_rows<D, C::BC>(kreg, Ks, tid);
+    store_cols<D, C::BC>(vreg, Vt, tid);
+    __syncthreads();
+  }
+  while (kt < ntiles) {
+    const int key0 = kt * C::BC;
+    const int nxt = next_visit(kt + 1);
+    if (nxt < ntiles) {  // in flight while this tile is computed
+      load_rows<D, C::BC>(kreg, Kp, a.sk.n, nxt * C::BC, p.N, tid);
+      load_cols<D, C::BC>(vreg, Vp, a.sv.n, nxt * C::BC, p.N, tid);
+    }
+    if (a.log && tid == 0) log_tile(a.log, log_row, key0);
+    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+
+#pragma unroll
+    for (int t = 0; t < C::NSUB; ++t) {
+      f32x16 s = f32x16{};
+      const bf16* kp = Ks + 32 * t * G::RPITCH + krow_off;
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) s = mfma(frag<bf16>(kp + 16 * kk), qf[kk], s);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * t + perm_row(r, hh);
+          if ((p.causal && key > my_q) || key >= kvalid) s[r] = -kInf;
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = half_max(mx) * sl2;
+      if (wave_any(mx > m_ref + C::kLag)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      }
+      const float m_use = m_ref == -kInf ? 0.f : m_ref;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_use));
+        s[r] = e;
+        l_run += e;
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 pf = pack8(s, c);
+        const int kc = 4 * t + 2 * c + hh;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          acc[db] = mfma(frag<bf16>(Vt + vrow_off[db] + 8 * (kc ^ vsw[db])), pf, acc[db]);
+      }
+    }
+    if (nxt < ntiles) {
+      __syncthreads();  // every wave is done with this tile
+      store_rows<D, C::BC>(kreg, Ks, tid);
+      store_cols<D, C::BC>(vreg, Vt, tid);
+      __syncthreads();
+    }
+    kt = nxt;
+  }
+
+  const float l_tot = half_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (my_q < p.N) {
+    char* obase = static_cast<char*>(a.o);
+    const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * hh;
+        const float v0 = acc[db][4 * g] * inv, v1 = acc[db][4 * g + 1] * inv;
+        const float v2 = acc[db][4 * g + 2] * inv, v3 = acc[db][4 * g + 3] * inv;
+        if (a.o_fp32) {
+          *reinterpret_cast<float4*>(obase + (orow + d0) * 4) = make_float4(v0, v1, v2, v3);
+        } else {
+          bf16x4 pk;
+          pk[0] = (bf16)v0;
+          pk[1] = (bf16)v1;
+          pk[2] = (bf16)v2;
+          pk[3] = (bf16)v3;
+          *reinterpret_cast<bf16x4*>(obase + (orow + d0) * 2) = pk;
+        }
+      }
+    if (hh == 0) {
+      const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -kInf;
+      a.lse[((int64_t)b * p.Hq + h) * p.N + my_q] = lse;
+    }
+  }
+}
+
+// fp32 inputs (reference-precision path) use the generic kernel above.
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const int64_t nqb = (a.p.N + 127) / 128;
@@ -207,9 +385,17 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+  const int64_t nqb = (a.p.N + FwdB<D>::BR - 1) / FwdB<D>::BR;
+  const int64_t grid = nqb * a.p.Hq * a.p.B;
+  hipLaunchKernelGGL((fwd_kernel_bf16<D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, hipStream_t s) {
   if (dtype == 0) {
-    return head_dim == 64 ? launch_fwd_t<bf16, 64>(a, s) : launch_fwd_t<bf16, 128>(a, s);
+    return head_dim == 64 ? launch_fwd_bf16<64>(a, s) : launch_fwd_bf16<128>(a, s);
   }
   return head_dim == 64 ? launch_fwd_t<float, 64>(a, s) : launch_fwd_t<float, 128>(a, s);
 }
