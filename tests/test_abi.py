@@ -1,0 +1,151 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/fa.h declares, and rejects invalid calls on the host before
+any HIP call (fake, never dereferenced pointer values are used)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import torch
+
+import exact_io_aware_29_amd as fa
+from exact_io_aware_29_amd import _abi
+
+# Every call below must be rejected by host-side validation; the pointer
+# values are fake. Where a GPU is visible these host checks are left to the
+# GPU suite, which exercises validation with real device buffers.
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fake-pointer ABI checks run on GPU-less hosts only")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|size_t|const char\*)\s+(fa_\w+)\s*\(", text)))
+
+
+def exported_symbols():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    return sorted({l.split()[-1] for l in out.splitlines() if " T " in l and "fa_" in l})
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert declared == sorted(_abi.SIGNATURES), "binding signatures out of date with fa.h"
+    exported = [s for s in exported_symbols() if s.startswith("fa_")]
+    assert exported == declared
+    lib = fa.library()
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"(FA_\w+)\s*=\s*(-?\d+)", text))
+    for name in ("FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_DTYPE", "FA_ERR_HEADDIM",
+                 "FA_ERR_GQA", "FA_ERR_STRIDE", "FA_ERR_ALIGN", "FA_ERR_WORKSPACE",
+                 "FA_ERR_HIP", "FA_ERR_MASK", "FA_ERR_SCALE", "FA_BF16", "FA_FP32"):
+        assert codes[name] == getattr(_abi, name), name
+    msgs = {fa.fa_strerror(c) for c in _abi.STATUS_CODES}
+    assert len(msgs) == len(_abi.STATUS_CODES)
+    assert fa.fa_strerror(12345) == "unknown status"
+
+
+def _params(**kw):
+    base = dict(batch=2, heads_q=4, heads_kv=2, seqlen=300, head_dim=64)
+    base.update(kw)
+    return fa.make_params(**base)
+
+
+def _strides(p, heads=None, eb=2, d=None):
+    d = d or p.head_dim
+    h = heads or p.heads_q
+    return _abi.Strides(h * p.seqlen * d, p.seqlen * d, d)
+
+
+P16, P32, P48, P64, P80 = (ctypes.c_void_p(x) for x in (0x1000, 0x2000, 0x3000, 0x4000, 0x5000))
+
+
+def _fwd(p, q=P16, k=P32, v=P48, o=P64, lse=P80, sq=None, sk=None, so=None, log=None):
+    lib = fa.library()
+    sq = sq or _strides(p)
+    sk = sk or _strides(p, p.heads_kv)
+    so = so or _strides(p)
+    st = lib.fa_fwd(ctypes.byref(p), q, sq, k, sk, v, sk, o, so, lse, log, None)
+    return st, lib.fa_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(head_dim=96), _abi.FA_ERR_HEADDIM),
+    (dict(head_dim=256), _abi.FA_ERR_HEADDIM),
+    (dict(heads_q=3), _abi.FA_ERR_GQA),
+    (dict(batch=0), _abi.FA_ERR_SHAPE),
+    (dict(seqlen=0), _abi.FA_ERR_SHAPE),
+    (dict(seqlen=-5), _abi.FA_ERR_SHAPE),
+    (dict(scale=0.0), _abi.FA_ERR_SCALE),
+    (dict(scale=-0.5), _abi.FA_ERR_SCALE),
+    (dict(scale=math.inf), _abi.FA_ERR_SCALE),
+    (dict(scale=math.nan), _abi.FA_ERR_SCALE),
+    (dict(dtype=7), _abi.FA_ERR_DTYPE),
+    (dict(dtype=_abi.FA_FP32, o_dtype=_abi.FA_BF16), _abi.FA_ERR_DTYPE),
+    (dict(block_mask=0x9000, block_mask_ld=2), _abi.FA_ERR_MASK),
+    (dict(batch=1 << 20, heads_q=1 << 10, heads_kv=1 << 10, seqlen=1 << 20), _abi.FA_ERR_SHAPE),
+])
+def test_fwd_rejects_bad_params(mut, code):
+    st, detail = _fwd(_params(**mut))
+    assert st == code, (st, detail)
+    assert detail
+
+
+def test_fwd_rejects_bad_pointers_and_strides():
+    p = _params()
+    assert _fwd(p, q=ctypes.c_void_p(0))[0] == _abi.FA_ERR_NULL
+    assert _fwd(p, lse=ctypes.c_void_p(0))[0] == _abi.FA_ERR_NULL
+    assert _fwd(p, k=ctypes.c_void_p(0x1008))[0] == _abi.FA_ERR_ALIGN
+    assert _fwd(p, o=ctypes.c_void_p(0x1004))[0] == _abi.FA_ERR_ALIGN
+    assert _fwd(p, lse=ctypes.c_void_p(0x1002))[0] == _abi.FA_ERR_ALIGN
+    assert _fwd(p, log=ctypes.c_void_p(0x1001))[0] == _abi.FA_ERR_ALIGN
+    bad = _abi.Strides(1, 1, 1)
+    assert _fwd(p, sq=bad)[0] == _abi.FA_ERR_STRIDE
+    neg = _abi.Strides(-64, 64, 64)
+    assert _fwd(p, sk=neg)[0] == _abi.FA_ERR_STRIDE
+    # bf16 strides must be multiples of 8 elements (16 bytes)
+    assert _fwd(_params(), sq=_abi.Strides(4, 4, 68))[0] == _abi.FA_ERR_STRIDE
+
+
+def test_bwd_validation():
+    lib = fa.library()
+    p = _params()
+    s, skv = _strides(p), _strides(p, p.heads_kv)
+    need = fa.fa_bwd_workspace_size(p)
+    assert need == 2 * 4 * 300 * 4
+
+    def call(p=p, ws=ctypes.c_void_p(0x7000), nbytes=need, ev=None):
+        return lib.fa_bwd(ctypes.byref(p), P16, s, P32, skv, P48, skv, P64, s, P80, s,
+                          ctypes.c_void_p(0x6000), P16, s, P32, skv, P48, skv, ws, nbytes,
+                          None, ev, None)
+
+    assert call(ws=ctypes.c_void_p(0)) == _abi.FA_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == _abi.FA_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x7008)) == _abi.FA_ERR_ALIGN
+    p32 = _params(dtype=_abi.FA_FP32, o_dtype=_abi.FA_FP32)
+    assert call(p=p32) == _abi.FA_ERR_DTYPE
+    ev = (ctypes.c_void_p * 4)(1, 2, None, 4)
+    assert call(ev=ctypes.cast(ev, ctypes.c_void_p)) == _abi.FA_ERR_NULL
+    assert "stage_events" in lib.fa_last_error_detail().decode()
+
+
+def test_size_queries():
+    p = _params(seqlen=4097)
+    nlb = 33
+    assert fa.fa_tile_log_words(p) == 2 * 4 * nlb * 2
+    assert fa.fa_bwd_workspace_size(p) == 2 * 4 * 4097 * 4
+    assert fa.fa_tile_log_words(_params(head_dim=80)) == 0
+    assert fa.fa_bwd_workspace_size(_params(heads_q=3)) == 0
