@@ -16,8 +16,8 @@ from exact_io_aware_29_amd import _abi
 # Every call below must be rejected by host-side validation; the pointer
 # values are fake. Where a GPU is visible these host checks are left to the
 # GPU suite, which exercises validation with real device buffers.
-pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
-                                reason="fake-pointer ABI checks run on GPU-less hosts only")
+no_gpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                 reason="fake-pointer ABI checks run on GPU-less hosts only")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
@@ -82,6 +82,7 @@ def _fwd(p, q=P16, k=P32, v=P48, o=P64, lse=P80, sq=None, sk=None, so=None, log=
     return st, lib.fa_last_error_detail().decode()
 
 
+@no_gpu_only
 @pytest.mark.parametrize("mut,code", [
     (dict(head_dim=96), _abi.FA_ERR_HEADDIM),
     (dict(head_dim=256), _abi.FA_ERR_HEADDIM),
@@ -104,6 +105,7 @@ def test_fwd_rejects_bad_params(mut, code):
     assert detail
 
 
+@no_gpu_only
 def test_fwd_rejects_bad_pointers_and_strides():
     p = _params()
     assert _fwd(p, q=ctypes.c_void_p(0))[0] == _abi.FA_ERR_NULL
@@ -120,6 +122,7 @@ def test_fwd_rejects_bad_pointers_and_strides():
     assert _fwd(_params(), sq=_abi.Strides(4, 4, 68))[0] == _abi.FA_ERR_STRIDE
 
 
+@no_gpu_only
 def test_bwd_validation():
     lib = fa.library()
     p = _params()
