@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
       trow[db] = (32 * db + lr) * G::TPITCH;
-      tsw[db] = (4 * db + (lr >> 3)) & 7;
+      tsw[db] = tswz<C::BQ>(32 * db + lr);
     }
 
     ColRegs<D, C::BQ> qreg, doreg;
@@ -191,6 +191,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
 
 #pragma unroll
       for (int u = 0; u < C::NQS; ++u) {
+        // Skip query sub-tiles that lie entirely above this wave's keys.
+        if (p.causal && q0b + 32 * u + 31 < k0 + 32 * w) continue;
         f32x16 s = f32x16{}, dp = f32x16{};
         const int ao = 32 * u * G::RPITCH + arow;
 #pragma unroll
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) {
     trow[db] = (32 * db + lr) * G::TPITCH;
-    tsw[db] = (4 * db + (lr >> 3)) & 7;
+    tsw[db] = tswz<C::BC>(32 * db + lr);
   }
 
   ColRegs<D, C::BC> kreg, vreg;
@@ -352,6 +354,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
+      const int sk0 = key0 + 32 * t;
+      if ((p.causal && sk0 > q0 + 32 * w + 31) || sk0 >= kvalid) continue;
       f32x16 st = f32x16{}, dpt = f32x16{};
       const int ao = 32 * t * G::RPITCH + arow;
 #pragma unroll

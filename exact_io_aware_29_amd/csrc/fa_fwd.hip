@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) {
     vrow_off[db] = (32 * db + lr) * G::TPITCH;
-    vsw[db] = (4 * db + (lr >> 3)) & 7;
+    vsw[db] = tswz<C::BC>(32 * db + lr);
   }
 
   RowRegs<D, C::BC> kreg;
@@ -296,6 +296,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
 
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
+      // Sub-tiles whose 32 keys are all masked for this wave's 32 rows
+      // (above the diagonal, or past the valid length) are skipped.
+      const int sk0 = key0 + 32 * t;
+      if ((p.causal && sk0 > q0 + 32 * w + 31) || sk0 >= kvalid) continue;
       f32x16 s = f32x16{};
       const bf16* kp = Ks + 32 * t * G::RPITCH + krow_off;
 #pragma unroll
@@ -307,10 +311,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
           if ((p.causal && key > my_q) || key >= kvalid) s[r] = -kInf;
         }
       }
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = half_max(mx) * sl2;
+      const float mx = half_max(tree_max16(s)) * sl2;
       if (wave_any(mx > m_ref + C::kLag)) {
         const float m_new = fmaxf(m_ref, mx);
         const float alpha = m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -323,11 +324,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
       }
       const float m_use = m_ref == -kInf ? 0.f : m_ref;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_use));
-        s[r] = e;
-        l_run += e;
-      }
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_use));
+      l_run += tree_sum16(s);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 pf = pack8(s, c);

@@ -109,9 +109,13 @@ namespace fa {
 //   * row-major with a 16-byte pad per row (pitch D + 8), read as MFMA A
 //     operands of 8 consecutive head-dim elements;
 //   * transposed (element (row, t) at [t][row]) with a 16-byte pad per
-//     transposed row and the 8-row chunks XOR-swizzled by (t / 8) % 8, read
-//     as A operands of 8 consecutive sequence rows. The swizzle makes both
-//     the 8-byte transposing writes and the 16-byte reads bank-conflict free.
+//     transposed row and its 8-row chunks XOR-swizzled by tswz(t), read as A
+//     operands of 8 consecutive sequence rows. gfx950's LDS has 64 four-byte
+//     banks; a 16-byte read is served 16 lanes at a time and an 8-byte write
+//     32 lanes at a time. Readers take 16 consecutive t at one chunk index,
+//     which the pad alone spreads over all banks (tswz is constant over
+//     them); writers take 8 column chunks x 2 row-chunk values x 2 halves,
+//     and tswz, built from bits 4.. of t, spreads those over all banks too.
 // ------------------------------------------------------------------------
 
 template <int D, int ROWS>
@@ -124,17 +128,31 @@ struct TileGeom {
   static_assert(ROWS * CPR % 256 == 0 && (ROWS / 4) * CPR % 256 == 0, "tile/thread mismatch");
 };
 
-// Position of the 16-byte chunk holding rows 8*kc .. 8*kc+7 of transposed
-// row t (element offset within the transposed tile).
-template <int TPITCH>
+// Chunk swizzle of transposed row t for a tile of ROWS sequence rows. With
+// 128 rows the writers' two row-chunk values differ in bit 0, so the
+// swizzle uses bits 1..2; with 64 rows they share one chunk and bits 0..2
+// are free.
+template <int ROWS>
+__device__ __forceinline__ int tswz(int t) {
+  if constexpr (ROWS == 128) {
+    return ((t >> 4) & 3) << 1;
+  } else {
+    static_assert(ROWS == 64, "transposed tiles hold 64 or 128 rows");
+    return (t >> 4) & 7;
+  }
+}
+
+// Element offset of the 16-byte chunk holding rows 8*kc .. 8*kc+7 of
+// transposed row t.
+template <int ROWS, int TPITCH>
 __device__ __forceinline__ int tposn(int t, int kc) {
-  return t * TPITCH + 8 * (kc ^ ((t >> 3) & 7));
+  return t * TPITCH + 8 * (kc ^ tswz<ROWS>(t));
 }
 
 // Thread -> (4-row group, 16-byte column chunk) for the transposing copy:
 // eight consecutive lanes take the eight column chunks of a 128-byte row
-// segment (coalesced), the next bit of the lane index selects the neighbour
-// row group, so a 16-lane write phase covers all 32 banks.
+// segment (coalesced global loads); the next lane bits select neighbouring
+// row groups (and, with 16 chunks per row, the other half of the row).
 template <int CPR>
 __device__ __forceinline__ void tmap(int g, int& rg, int& colc) {
   if constexpr (CPR == 8) {
@@ -212,7 +230,7 @@ __device__ __forceinline__ void store_cols(const ColRegs<D, ROWS>& r, bf16* dst,
       const uint32_t v0 = (x[0].d[e >> 1] >> sh) & 0xffffu, v1 = (x[1].d[e >> 1] >> sh) & 0xffffu;
       const uint32_t v2 = (x[2].d[e >> 1] >> sh) & 0xffffu, v3 = (x[3].d[e >> 1] >> sh) & 0xffffu;
       const int t = colc * 8 + e;
-      *reinterpret_cast<uint2*>(dst + tposn<G::TPITCH>(t, rg >> 1) + 4 * (rg & 1)) =
+      *reinterpret_cast<uint2*>(dst + tposn<ROWS, G::TPITCH>(t, rg >> 1) + 4 * (rg & 1)) =
           make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
     }
   }
