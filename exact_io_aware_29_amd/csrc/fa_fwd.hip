@@ -204,11 +204,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 template <int D>
 struct FwdB {
   static constexpr int BR = 128;                  // rows per workgroup (4 waves x 32)
-  static constexpr int BC = D == 64 ? 128 : 64;   // keys per tile
+  static constexpr int BC = 64;                   // keys per tile
   static constexpr int NKK = D / 16;
   static constexpr int NSUB = BC / 32;
   static constexpr int NDB = D / 32;
-  using G = TileGeom<D, BC>;
+  using T = SwzTile<D, BC>;
   // Running maxima are allowed to lag the true row maximum by up to this
   // much (log2 units): P~ then stays below 2^8, which bf16 and the fp32 sums
   // hold exactly as well as values below 1, and the O rescale (one multiply
@@ -219,12 +219,13 @@ struct FwdB {
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   using C = FwdB<D>;
-  using G = typename C::G;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[C::BC * G::RPITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * G::TPITCH];
+  using T = typename C::T;
+  // Two stages of (K tile | V tile), filled by DMA while the other is read.
+  __shared__ __attribute__((aligned(1024))) char smem[2][2 * T::BYTES];
 
   const Problem& p = a.p;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
 
   const int nqb = (p.N + C::BR - 1) / C::BR;
@@ -236,10 +237,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   const int q0 = qb * C::BR;
   const int my_q = q0 + 32 * w + lr;
 
-  const bf16* Kp = static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h;
-  const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
+  const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;  // row strides in bytes
+  const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
+                             (uint32_t)(p.N - 1) * ksb + 2 * D);
+  const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
+                             (uint32_t)(p.N - 1) * vsb + 2 * D);
 
-  const int kvalid = valid_keys(p.seqlens, b, p.N);
+  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
   const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
   const int ntiles = (kend + C::BC - 1) / C::BC;
 
@@ -252,6 +256,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = frag_g(qrow + 16 * kk, ok);
   }
 
+  int kvo[T::NLD], vvo[T::NLD];
+  dma_offsets<D, C::BC>(kvo, ksb, w, lane);
+  dma_offsets<D, C::BC>(vvo, vsb, w, lane);
+  int roff[C::NKK], troff[C::NDB][2];
+  row_offsets<D, C::BC>(roff, lr, hh);
+  tr_offsets<D, C::BC>(troff, lane);
+
   f32x16 acc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
@@ -261,38 +272,30 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   const int64_t log_row =
       a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
 
-  const int krow_off = swap_bits23(lr) * G::RPITCH + 8 * hh;
-  int vrow_off[C::NDB], vsw[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    vrow_off[db] = (32 * db + lr) * G::TPITCH;
-    vsw[db] = tswz<C::BC>(32 * db + lr);
-  }
-
-  RowRegs<D, C::BC> kreg;
-  ColRegs<D, C::BC> vreg;
   auto next_visit = [&](int kt) {
     while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
     return kt;
   };
+  auto issue = [&](int kt, int st) {
+    dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, smem[st], w);
+    dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, smem[st] + T::BYTES, w);
+  };
 
   int kt = next_visit(0);
+  int st = 0;
   if (kt < ntiles) {
-    load_rows<D, C::BC>(kreg, Kp, a.sk.n, kt * C::BC, p.N, tid);
-    load_cols<D, C::BC>(vreg, Vp, a.sv.n, kt * C::BC, p.N, tid);
-    store_rows<D, C::BC>(kreg, Ks, tid);
-    store_cols<D, C::BC>(vreg, Vt, tid);
+    issue(kt, 0);
+    wait_dma();
     __syncthreads();
   }
   while (kt < ntiles) {
     const int key0 = kt * C::BC;
     const int nxt = next_visit(kt + 1);
-    if (nxt < ntiles) {  // in flight while this tile is computed
-      load_rows<D, C::BC>(kreg, Kp, a.sk.n, nxt * C::BC, p.N, tid);
-      load_cols<D, C::BC>(vreg, Vp, a.sv.n, nxt * C::BC, p.N, tid);
-    }
+    if (nxt < ntiles) issue(nxt, st ^ 1);  // lands while this tile is computed
     if (a.log && tid == 0) log_tile(a.log, log_row, key0);
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+    const char* Ks = smem[st];
+    const char* Vs = smem[st] + T::BYTES;
 
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
@@ -301,13 +304,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
       const int sk0 = key0 + 32 * t;
       if ((p.causal && sk0 > q0 + 32 * w + 31) || sk0 >= kvalid) continue;
       f32x16 s = f32x16{};
-      const bf16* kp = Ks + 32 * t * G::RPITCH + krow_off;
+      const char* kp = Ks + 32 * t * T::RB;
 #pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) s = mfma(frag<bf16>(kp + 16 * kk), qf[kk], s);
+      for (int kk = 0; kk < C::NKK; ++kk) s = mfma(lds_row(kp, roff[kk]), qf[kk], s);
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * t + perm_row(r, hh);
+          const int key = sk0 + perm_row(r, hh);
           if ((p.causal && key > my_q) || key >= kvalid) s[r] = -kInf;
         }
       }
@@ -329,18 +332,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 pf = pack8(s, c);
-        const int kc = 4 * t + 2 * c + hh;
+        const char* vp = Vs + (32 * t + 16 * c) * T::RB;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
-          acc[db] = mfma(frag<bf16>(Vt + vrow_off[db] + 8 * (kc ^ vsw[db])), pf, acc[db]);
+          acc[db] = mfma(lds_tr(vp, troff[db][0], troff[db][1]), pf, acc[db]);
       }
     }
     if (nxt < ntiles) {
-      __syncthreads();  // every wave is done with this tile
-      store_rows<D, C::BC>(kreg, Ks, tid);
-      store_cols<D, C::BC>(vreg, Vt, tid);
-      __syncthreads();
+      wait_dma();
+      __syncthreads();  // next tile landed everywhere; this tile is no longer read
     }
+    st ^= 1;
     kt = nxt;
   }
 

@@ -251,3 +251,135 @@ __device__ __forceinline__ void store_rows_t(const ColRegs<D, ROWS>& r, bf16* ds
 }
 
 }  // namespace fa
+
+namespace fa {
+
+// ------------------------------------------------------------------------
+// DMA-staged tiles (bf16 kernels).
+//
+// Tiles of ROWS sequence rows x D bf16 live in LDS row-major and unpadded;
+// the sixteen-byte chunk c of row r sits at chunk position c ^ swz(r). They
+// are filled by buffer loads that write LDS directly (64 lanes x 16 bytes =
+// one contiguous KiB per wave instruction), so a lane's global source is
+// chosen to be the chunk that belongs at its LDS position. Buffer loads
+// return zero beyond the tensor's last row, which zero-fills tail tiles
+// without predication.
+//
+// Operands are read back in two ways (both bank-conflict free on gfx950's
+// 64 LDS banks with this swizzle, as measured):
+//   * 16-byte reads of 8 consecutive head-dim elements of one row (MFMA
+//     A operands whose rows are sequence rows);
+//   * ds_read_b64_tr_b16 transposing reads, which give each lane 4
+//     consecutive sequence rows of one head-dim column (MFMA A operands
+//     whose rows are head-dim indices). Within each 16-lane group, output
+//     lane i receives element i % 4 of the 8 bytes loaded by group lane
+//     4 e + i / 4, for e = 0..3; loader lane 4 e + a therefore reads row
+//     base + e at columns 4 a .. 4 a + 3 of a 16-column slice.
+// ------------------------------------------------------------------------
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+#define FA_LDS __attribute__((address_space(3)))
+
+// Raw buffer over [base, base + nbytes); the dword-3 constant selects the
+// plain 32-bit data format used for untyped buffer access on this chip.
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+
+template <int D, int ROWS>
+struct SwzTile {
+  static constexpr int RB = 2 * D;            // bytes per row
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int BYTES = ROWS * RB;
+  static constexpr int NLD = BYTES / (256 * 16);  // DMA loads per thread
+  static_assert(BYTES % (256 * 16) == 0, "tile must be a whole number of workgroup loads");
+  static_assert(ROWS % 16 == 0, "operand fetch works on 16-row groups");
+  // Chunk swizzle: a bijection on the row's chunk index chosen so that 16
+  // consecutive rows at one chunk, and 4 consecutive rows x 4 consecutive
+  // chunks, each spread over all 64 banks.
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (D == 64) {
+      return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    } else {
+      return ((r & 3) << 2) | ((r >> 2) & 3);
+    }
+  }
+  __device__ static __forceinline__ int off(int r, int c) { return r * RB + 16 * (c ^ swz(r)); }
+};
+
+// Per-lane global byte offsets (relative to the tile's first row) of the
+// DMA loads that fill one tile; computed once per kernel.
+template <int D, int ROWS, int NL>
+__device__ __forceinline__ void dma_offsets(int (&voff)[NL], int stride_bytes, int w, int lane) {
+  using T = SwzTile<D, ROWS>;
+  static_assert(NL == T::NLD, "one offset per DMA load");
+#pragma unroll
+  for (int i = 0; i < T::NLD; ++i) {
+    const int p = (i * 4 + w) * 64 + lane;  // 16-byte LDS position
+    const int r = p / T::CPR, pc = p % T::CPR;
+    voff[i] = r * stride_bytes + 16 * (pc ^ T::swz(r));
+  }
+}
+
+template <int D, int ROWS, int NL>
+__device__ __forceinline__ void dma_tile(Rsrc rs, const int (&voff)[NL], uint32_t soff, char* tile,
+                                         int w) {
+  using T = SwzTile<D, ROWS>;
+  static_assert(NL == T::NLD, "one offset per DMA load");
+#pragma unroll
+  for (int i = 0; i < T::NLD; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + (i * 4 + w) * 1024), 16,
+                                             voff[i], soff, 0, 0);
+}
+
+// This wave's DMA loads have landed in LDS.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte row operand at byte offset `off` of an LDS tile.
+__device__ __forceinline__ bf16x8 lds_row(const char* tile, int off) {
+  return *reinterpret_cast<const bf16x8*>(tile + off);
+}
+
+// Transposed operand: two transposing reads (slots 0-3 and 4-7).
+__device__ __forceinline__ bf16x8 lds_tr(const char* tile, int off0, int off1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(tile + off0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(tile + off1));
+  const i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Lane offsets for the row operand of a 32-row MFMA block whose rows are
+// loaded in swap_bits23 order: chunk 2 kk + h of row swap_bits23(lane % 32).
+template <int D, int ROWS, int NK>
+__device__ __forceinline__ void row_offsets(int (&off)[NK], int lr, int hh) {
+  static_assert(NK == D / 16, "one offset per 16-wide head-dim step");
+  using T = SwzTile<D, ROWS>;
+  const int r = swap_bits23(lr);
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) off[kk] = T::off(r, 2 * kk + hh);
+}
+
+// Lane offsets for the transposed operand: output lane l (row = head-dim
+// index 32 db + l % 32) gets sequence rows 16 c + 8 h + 4 j + 0..3 (slots
+// 4 j .. 4 j + 3). As a loader, lane l of 16-lane group g reads row
+// 8 h + 4 j + (q >> 2) at head-dim 32 db + 16 (g & 1) + 4 (q & 3).
+// The sixteen-row base 16 c (+ 32 t) is added as an immediate.
+template <int D, int ROWS, int NB>
+__device__ __forceinline__ void tr_offsets(int (&off)[NB][2], int lane) {
+  static_assert(NB == D / 32, "one offset pair per 32-row head-dim block");
+  using T = SwzTile<D, ROWS>;
+  const int g = lane >> 4, q = lane & 15, hh = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * hh + 4 * j + (q >> 2);
+      const int d = 32 * db + 16 * (g & 1) + 4 * (q & 3);
+      off[db][j] = r * T::RB + 16 * ((d >> 3) ^ T::swz(r)) + 2 * (d & 7);
+    }
+}
+
+}  // namespace fa
