@@ -80,22 +80,21 @@ struct DkdvCfg {
   static constexpr int NQS = BQ / 32;
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
-  using G = TileGeom<D, BQ>;
+  using T = SwzTile<D, BQ>;
 };
 
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<D>;
-  using G = typename C::G;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[C::BQ * G::RPITCH];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[C::BQ * G::RPITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[D * G::TPITCH];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[D * G::TPITCH];
-  __shared__ __attribute__((aligned(16))) float lse_s[C::BQ];
-  __shared__ __attribute__((aligned(16))) float dvec_s[C::BQ];
+  using T = typename C::T;
+  // Two stages of (Q tile | dO tile), filled by DMA while the other is read.
+  __shared__ __attribute__((aligned(1024))) char smem[2][2 * T::BYTES];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][C::BQ];
+  __shared__ __attribute__((aligned(16))) float dvec_s[2][C::BQ];
 
   const Problem& p = a.p;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
   const int nkb = (p.N + C::BK - 1) / C::BK;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -128,7 +127,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     dvt[db] = f32x16{};
   }
 
-  const int kvalid = valid_keys(p.seqlens, b, p.N);
+  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
   if (k0 < kvalid) {  // else every key of the block is masked: dK = dV = 0
     // Steps run over (query head of the group) x (query block); rows above
     // the diagonal see none of these keys under the causal mask.
@@ -139,23 +138,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
       while (st < nsteps && !block_on(p.bm, p.bm_ld, (qfirst + st % nq) * C::BQ, k0)) ++st;
       return st;
     };
-    const int arow = swap_bits23(lr) * G::RPITCH + 8 * hh;
-    int trow[C::NDB], tsw[C::NDB];
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      trow[db] = (32 * db + lr) * G::TPITCH;
-      tsw[db] = tswz<C::BQ>(32 * db + lr);
-    }
+    const int qsb = 2 * (int)a.sq.n, dsb = 2 * (int)a.sdo.n;
+    int qvo[T::NLD], dvo[T::NLD];
+    dma_offsets<D, C::BQ>(qvo, qsb, w, lane);
+    dma_offsets<D, C::BQ>(dvo, dsb, w, lane);
+    int roff[C::NKK], troff[C::NDB][2];
+    row_offsets<D, C::BQ>(roff, lr, hh);
+    tr_offsets<D, C::BQ>(troff, lane);
 
-    ColRegs<D, C::BQ> qreg, doreg;
     float lse_r = 0.f, dvec_r = 0.f;
-    auto fetch = [&](int st) {
-      const int h = hk * p.G + st / nq;
-      const int q0b = (qfirst + st % nq) * C::BQ;
-      load_cols<D, C::BQ>(qreg, static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h, a.sq.n,
-                          q0b, p.N, tid);
-      load_cols<D, C::BQ>(doreg, static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
-                          a.sdo.n, q0b, p.N, tid);
+    auto issue = [&](int sidx, int stage) {
+      const int h = hk * p.G + sidx / nq;
+      const int q0b = (qfirst + sidx % nq) * C::BQ;
+      const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
+                                 (uint32_t)(p.N - 1) * qsb + 2 * D);
+      const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
+                                 (uint32_t)(p.N - 1) * dsb + 2 * D);
+      dma_tile<D, C::BQ>(qrs, qvo, (uint32_t)q0b * qsb, smem[stage], w);
+      dma_tile<D, C::BQ>(drs, dvo, (uint32_t)q0b * dsb, smem[stage] + T::BYTES, w);
       if (tid < C::BQ) {
         const int qi = q0b + tid;
         const int64_t off = ((int64_t)b * p.Hq + h) * p.N + qi;
@@ -163,48 +163,49 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         dvec_r = qi < p.N ? a.dvec[off] : 0.f;
       }
     };
-    auto stage = [&]() {
-      store_rows_t<D, C::BQ>(qreg, Qs, tid);
-      store_cols<D, C::BQ>(qreg, Qt, tid);
-      store_rows_t<D, C::BQ>(doreg, dOs, tid);
-      store_cols<D, C::BQ>(doreg, dOt, tid);
+    auto put_rowstats = [&](int stage) {
       if (tid < C::BQ) {
-        lse_s[tid] = lse_r;
-        dvec_s[tid] = dvec_r;
+        lse_s[stage][tid] = lse_r;
+        dvec_s[stage][tid] = dvec_r;
       }
     };
 
-    int st = next_step(0);
-    if (st < nsteps) {
-      fetch(st);
-      stage();
+    int sidx = next_step(0);
+    int stage = 0;
+    if (sidx < nsteps) {
+      issue(sidx, 0);
+      put_rowstats(0);
+      wait_dma();
       __syncthreads();
     }
-    while (st < nsteps) {
-      const int h = hk * p.G + st / nq;
-      const int q0b = (qfirst + st % nq) * C::BQ;
-      const int nx = next_step(st + 1);
-      if (nx < nsteps) fetch(nx);  // in flight during this step
+    while (sidx < nsteps) {
+      const int h = hk * p.G + sidx / nq;
+      const int q0b = (qfirst + sidx % nq) * C::BQ;
+      const int nx = next_step(sidx + 1);
+      if (nx < nsteps) issue(nx, stage ^ 1);  // lands during this step
       if (a.log_kv && tid == 0)
         log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
       const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid);
+      const char* Qs = smem[stage];
+      const char* dOs = smem[stage] + T::BYTES;
 
 #pragma unroll
       for (int u = 0; u < C::NQS; ++u) {
         // Skip query sub-tiles that lie entirely above this wave's keys.
         if (p.causal && q0b + 32 * u + 31 < k0 + 32 * w) continue;
         f32x16 s = f32x16{}, dp = f32x16{};
-        const int ao = 32 * u * G::RPITCH + arow;
+        const char* qp = Qs + 32 * u * T::RB;
+        const char* dop = dOs + 32 * u * T::RB;
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk) {
-          s = mfma(frag<bf16>(Qs + ao + 16 * kk), kf[kk], s);
-          dp = mfma(frag<bf16>(dOs + ao + 16 * kk), vf[kk], dp);
+          s = mfma(lds_row(qp, roff[kk]), kf[kk], s);
+          dp = mfma(lds_row(dop, roff[kk]), vf[kk], dp);
         }
         // Register r holds query row 32u + perm_row(r, hh) of this step.
-        const f32x4* l4 = reinterpret_cast<const f32x4*>(lse_s + 32 * u + 8 * hh);
-        const f32x4* d4 = reinterpret_cast<const f32x4*>(dvec_s + 32 * u + 8 * hh);
-        f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
-        f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
+        const f32x4* l4 = reinterpret_cast<const f32x4*>(lse_s[stage] + 32 * u + 8 * hh);
+        const f32x4* d4 = reinterpret_cast<const f32x4*>(dvec_s[stage] + 32 * u + 8 * hh);
+        const f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
+        const f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[r >> 2][r & 3]));
@@ -219,21 +220,21 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         for (int c = 0; c < 2; ++c) {
           const bf16x8 pf = pack8(s, c);
           const bf16x8 dsf = pack8(dp, c);
-          const int kc = 4 * u + 2 * c + hh;
+          const int rb = (32 * u + 16 * c) * T::RB;
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const int to = trow[db] + 8 * (kc ^ tsw[db]);
-            dvt[db] = mfma(frag<bf16>(dOt + to), pf, dvt[db]);
-            dkt[db] = mfma(frag<bf16>(Qt + to), dsf, dkt[db]);
+            dvt[db] = mfma(lds_tr(dOs + rb, troff[db][0], troff[db][1]), pf, dvt[db]);
+            dkt[db] = mfma(lds_tr(Qs + rb, troff[db][0], troff[db][1]), dsf, dkt[db]);
           }
         }
       }
       if (nx < nsteps) {
-        __syncthreads();
-        stage();
+        put_rowstats(stage ^ 1);
+        wait_dma();
         __syncthreads();
       }
-      st = nx;
+      stage ^= 1;
+      sidx = nx;
     }
   }
 
@@ -261,24 +262,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
 
 template <int D>
 struct DqCfg {
-  static constexpr int BR = 128;       // query rows per workgroup
-  static constexpr int BC = 8192 / D;  // keys per tile (128 or 64)
+  static constexpr int BR = 128;  // query rows per workgroup
+  static constexpr int BC = 64;   // keys per tile
   static constexpr int NSUB = BC / 32;
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
-  using G = TileGeom<D, BC>;
+  using T = SwzTile<D, BC>;
 };
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D>;
-  using G = typename C::G;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[C::BC * G::RPITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[C::BC * G::RPITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[D * G::TPITCH];
+  using T = typename C::T;
+  // Two stages of (K tile | V tile); K^T operands come from the K tile
+  // through transposing reads.
+  __shared__ __attribute__((aligned(1024))) char smem[2][2 * T::BYTES];
 
   const Problem& p = a.p;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
   const int nqb = (p.N + C::BR - 1) / C::BR;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -290,8 +292,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int my_q = q0 + 32 * w + lr;
   const float sl2 = p.scale_l2;
 
-  const bf16* Kp = static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h;
-  const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
+  const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;
+  const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
+                             (uint32_t)(p.N - 1) * ksb + 2 * D);
+  const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
+                             (uint32_t)(p.N - 1) * vsb + 2 * D);
 
   const bool qok = my_q < p.N;
   bf16x8 qf[C::NKK], dof[C::NKK];
@@ -309,11 +314,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const float lse2 = qok ? lse2_of(a.lse[rowstat]) : kInf;
   const float dq_d = qok ? a.dvec[rowstat] : 0.f;
 
+  int kvo[T::NLD], vvo[T::NLD];
+  dma_offsets<D, C::BC>(kvo, ksb, w, lane);
+  dma_offsets<D, C::BC>(vvo, vsb, w, lane);
+  int roff[C::NKK], troff[C::NDB][2];
+  row_offsets<D, C::BC>(roff, lr, hh);
+  tr_offsets<D, C::BC>(troff, lane);
+
   f32x16 acc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
-  const int kvalid = valid_keys(p.seqlens, b, p.N);
+  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
   const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
   const int ntiles = (kend + C::BC - 1) / C::BC;
   const int64_t log_row =
@@ -322,52 +334,43 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
     return kt;
   };
-  const int arow = swap_bits23(lr) * G::RPITCH + 8 * hh;
-  int trow[C::NDB], tsw[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    trow[db] = (32 * db + lr) * G::TPITCH;
-    tsw[db] = tswz<C::BC>(32 * db + lr);
-  }
-
-  ColRegs<D, C::BC> kreg, vreg;
-  auto stage = [&]() {
-    store_rows_t<D, C::BC>(kreg, Ks, tid);
-    store_cols<D, C::BC>(kreg, Kt, tid);
-    store_rows_t<D, C::BC>(vreg, Vs, tid);
+  auto issue = [&](int kt, int stage) {
+    dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, smem[stage], w);
+    dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, smem[stage] + T::BYTES, w);
   };
+
   int kt = next_visit(0);
+  int stage = 0;
   if (kt < ntiles) {
-    load_cols<D, C::BC>(kreg, Kp, a.sk.n, kt * C::BC, p.N, tid);
-    load_cols<D, C::BC>(vreg, Vp, a.sv.n, kt * C::BC, p.N, tid);
-    stage();
+    issue(kt, 0);
+    wait_dma();
     __syncthreads();
   }
   while (kt < ntiles) {
     const int key0 = kt * C::BC;
     const int nxt = next_visit(kt + 1);
-    if (nxt < ntiles) {
-      load_cols<D, C::BC>(kreg, Kp, a.sk.n, nxt * C::BC, p.N, tid);
-      load_cols<D, C::BC>(vreg, Vp, a.sv.n, nxt * C::BC, p.N, tid);
-    }
+    if (nxt < ntiles) issue(nxt, stage ^ 1);
     if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+    const char* Ks = smem[stage];
+    const char* Vs = smem[stage] + T::BYTES;
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
       const int sk0 = key0 + 32 * t;
       if ((p.causal && sk0 > q0 + 32 * w + 31) || sk0 >= kvalid) continue;
       f32x16 st = f32x16{}, dpt = f32x16{};
-      const int ao = 32 * t * G::RPITCH + arow;
+      const char* kp = Ks + 32 * t * T::RB;
+      const char* vp = Vs + 32 * t * T::RB;
 #pragma unroll
       for (int kk = 0; kk < C::NKK; ++kk) {
-        st = mfma(frag<bf16>(Ks + ao + 16 * kk), qf[kk], st);
-        dpt = mfma(frag<bf16>(Vs + ao + 16 * kk), dof[kk], dpt);
+        st = mfma(lds_row(kp, roff[kk]), qf[kk], st);
+        dpt = mfma(lds_row(vp, roff[kk]), dof[kk], dpt);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
         if (need_mask) {
-          const int key = key0 + 32 * t + perm_row(r, hh);
+          const int key = sk0 + perm_row(r, hh);
           if ((p.causal && key > my_q) || key >= kvalid) pv = 0.f;
         }
         dpt[r] = pv * (dpt[r] - dq_d);
@@ -375,17 +378,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 dsf = pack8(dpt, c);
-        const int kc = 4 * t + 2 * c + hh;
+        const char* ktp = Ks + (32 * t + 16 * c) * T::RB;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
-          acc[db] = mfma(frag<bf16>(Kt + trow[db] + 8 * (kc ^ tsw[db])), dsf, acc[db]);
+          acc[db] = mfma(lds_tr(ktp, troff[db][0], troff[db][1]), dsf, acc[db]);
       }
     }
     if (nxt < ntiles) {
-      __syncthreads();
-      stage();
+      wait_dma();
       __syncthreads();
     }
+    stage ^= 1;
     kt = nxt;
   }
 

@@ -324,11 +324,10 @@ __device__ __forceinline__ void dma_offsets(int (&voff)[NL], int stride_bytes, i
   }
 }
 
-template <int D, int ROWS, int NL>
-__device__ __forceinline__ void dma_tile(Rsrc rs, const int (&voff)[NL], uint32_t soff, char* tile,
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_tile(Rsrc rs, const int* voff, uint32_t soff, char* tile,
                                          int w) {
   using T = SwzTile<D, ROWS>;
-  static_assert(NL == T::NLD, "one offset per DMA load");
 #pragma unroll
   for (int i = 0; i < T::NLD; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + (i * 4 + w) * 1024), 16,
