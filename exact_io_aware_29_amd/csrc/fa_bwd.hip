@@ -196,10 +196,21 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         f32x16 s = f32x16{}, dp = f32x16{};
         const char* qp = Qs + 32 * u * T::RB;
         const char* dop = dOs + 32 * u * T::RB;
+        // Operands are fetched four at a time ahead of their products so the
+        // LDS latency overlaps the matrix pipe.
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) {
-          s = mfma(lds_row(qp, roff[kk]), kf[kk], s);
-          dp = mfma(lds_row(dop, roff[kk]), vf[kk], dp);
+        for (int k4 = 0; k4 < C::NKK; k4 += 4) {
+          bf16x8 qa[4], da[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            qa[i] = lds_row(qp, roff[k4 + i]);
+            da[i] = lds_row(dop, roff[k4 + i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s = mfma(qa[i], kf[k4 + i], s);
+            dp = mfma(da[i], vf[k4 + i], dp);
+          }
         }
         // Register r holds query row 32u + perm_row(r, hh) of this step.
         const f32x4* l4 = reinterpret_cast<const f32x4*>(lse_s[stage] + 32 * u + 8 * hh);
@@ -207,15 +218,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         const f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
         const f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[r >> 2][r & 3]));
-          if (need_mask) {
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[r >> 2][r & 3]));
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const int qi = q0b + 32 * u + perm_row(r, hh);
-            if ((p.causal && my_k > qi) || my_k >= kvalid) pv = 0.f;
+            if ((p.causal && my_k > qi) || my_k >= kvalid) s[r] = 0.f;
           }
-          s[r] = pv;
-          dp[r] = pv * (dp[r] - dv4[r >> 2][r & 3]);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dv4[r >> 2][r & 3]);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const bf16x8 pf = pack8(s, c);
@@ -362,19 +374,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const char* kp = Ks + 32 * t * T::RB;
       const char* vp = Vs + 32 * t * T::RB;
 #pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) {
-        st = mfma(lds_row(kp, roff[kk]), qf[kk], st);
-        dpt = mfma(lds_row(vp, roff[kk]), dof[kk], dpt);
+      for (int k4 = 0; k4 < C::NKK; k4 += 4) {
+        bf16x8 ka[4], va[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ka[i] = lds_row(kp, roff[k4 + i]);
+          va[i] = lds_row(vp, roff[k4 + i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          st = mfma(ka[i], qf[k4 + i], st);
+          dpt = mfma(va[i], dof[k4 + i], dpt);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
-        if (need_mask) {
+      for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int key = sk0 + perm_row(r, hh);
-          if ((p.causal && key > my_q) || key >= kvalid) pv = 0.f;
+          if ((p.causal && key > my_q) || key >= kvalid) st[r] = 0.f;
         }
-        dpt[r] = pv * (dpt[r] - dq_d);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (dpt[r] - dq_d);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 dsf = pack8(dpt, c);

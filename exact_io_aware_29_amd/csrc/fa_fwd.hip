@@ -297,46 +297,67 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     const char* Ks = smem[st];
     const char* Vs = smem[st] + T::BYTES;
 
+    // One straight-line block per tile (no per-sub-tile branches), so the
+    // compiler can overlap one sub-tile's exponentials with its neighbour's
+    // matrix products: all S^T products, one max and lazy-rescale test for
+    // the whole tile, then exp / pack / PV per sub-tile.
+    f32x16 s[C::NSUB];
+    // Raised priority while this wave feeds the matrix pipe, so that waves
+    // sharing the SIMD fill the VALU between its products.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
-      // Sub-tiles whose 32 keys are all masked for this wave's 32 rows
-      // (above the diagonal, or past the valid length) are skipped.
-      const int sk0 = key0 + 32 * t;
-      if ((p.causal && sk0 > q0 + 32 * w + 31) || sk0 >= kvalid) continue;
-      f32x16 s = f32x16{};
+      s[t] = f32x16{};
       const char* kp = Ks + 32 * t * T::RB;
 #pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) s = mfma(lds_row(kp, roff[kk]), qf[kk], s);
-      if (need_mask) {
+      for (int k4 = 0; k4 < C::NKK; k4 += 4) {
+        bf16x8 ka[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ka[i] = lds_row(kp, roff[k4 + i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[t] = mfma(ka[i], qf[k4 + i], s[t]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (need_mask) {
+#pragma unroll
+      for (int t = 0; t < C::NSUB; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = sk0 + perm_row(r, hh);
-          if ((p.causal && key > my_q) || key >= kvalid) s[r] = -kInf;
+          const int key = key0 + 32 * t + perm_row(r, hh);
+          if ((p.causal && key > my_q) || key >= kvalid) s[t][r] = -kInf;
         }
-      }
-      const float mx = half_max(tree_max16(s)) * sl2;
-      if (wave_any(mx > m_ref + C::kLag)) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
+    }
+    float mx = tree_max16(s[0]);
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+    for (int t = 1; t < C::NSUB; ++t) mx = fmaxf(mx, tree_max16(s[t]));
+    mx = half_max(mx) * sl2;
+    if (wave_any(mx > m_ref + C::kLag)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      }
-      const float m_use = m_ref == -kInf ? 0.f : m_ref;
+      for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_use));
-      l_run += tree_sum16(s);
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    const float m_use = m_ref == -kInf ? 0.f : m_ref;
+#pragma unroll
+    for (int t = 0; t < C::NSUB; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, -m_use));
+      l_run += tree_sum16(s[t]);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 pf = pack8(s, c);
+        const bf16x8 pf = pack8(s[t], c);
         const char* vp = Vs + (32 * t + 16 * c) * T::RB;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
           acc[db] = mfma(lds_tr(vp, troff[db][0], troff[db][1]), pf, acc[db]);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (nxt < ntiles) {
       wait_dma();
