@@ -78,6 +78,7 @@ struct DkdvCfg {
   static constexpr int BK = 128;       // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 8192 / D;  // query rows staged per step
   static constexpr int NQS = BQ / 32;
+  static constexpr int NG = 2;         // sub-tiles per straight-line group
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
   using T = SwzTile<D, BQ>;
@@ -104,6 +105,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
   const int k0 = kb * C::BK;
   const int my_k = k0 + 32 * w + lr;
   const float sl2 = p.scale_l2;
+  const bool causal = p.causal != 0;
 
   const bf16* Kp = static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h;
   const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
@@ -189,54 +191,70 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
       const char* Qs = smem[stage];
       const char* dOs = smem[stage] + T::BYTES;
 
+      // Straight-line step (no per-sub-tile branches): all S and dP products,
+      // one uniform mask block, then P / dS and the dV, dK products, so the
+      // compiler can overlap one sub-tile's exponentials with another's
+      // matrix products.
 #pragma unroll
-      for (int u = 0; u < C::NQS; ++u) {
-        // Skip query sub-tiles that lie entirely above this wave's keys.
-        if (p.causal && q0b + 32 * u + 31 < k0 + 32 * w) continue;
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const char* qp = Qs + 32 * u * T::RB;
-        const char* dop = dOs + 32 * u * T::RB;
-        // Operands are fetched four at a time ahead of their products so the
-        // LDS latency overlaps the matrix pipe.
+      for (int g0 = 0; g0 < C::NQS; g0 += C::NG) {
+        f32x16 s[C::NG], dp[C::NG];
 #pragma unroll
-        for (int k4 = 0; k4 < C::NKK; k4 += 4) {
-          bf16x8 qa[4], da[4];
+        for (int uu = 0; uu < C::NG; ++uu) {
+          s[uu] = f32x16{};
+          dp[uu] = f32x16{};
+          const char* qp = Qs + 32 * (g0 + uu) * T::RB;
+          const char* dop = dOs + 32 * (g0 + uu) * T::RB;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            qa[i] = lds_row(qp, roff[k4 + i]);
-            da[i] = lds_row(dop, roff[k4 + i]);
-          }
+          for (int k4 = 0; k4 < C::NKK; k4 += 4) {
+            bf16x8 qa[4], da[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            s = mfma(qa[i], kf[k4 + i], s);
-            dp = mfma(da[i], vf[k4 + i], dp);
+            for (int i = 0; i < 4; ++i) {
+              qa[i] = lds_row(qp, roff[k4 + i]);
+              da[i] = lds_row(dop, roff[k4 + i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              s[uu] = mfma(qa[i], kf[k4 + i], s[uu]);
+              dp[uu] = mfma(da[i], vf[k4 + i], dp[uu]);
+            }
           }
         }
-        // Register r holds query row 32u + perm_row(r, hh) of this step.
-        const f32x4* l4 = reinterpret_cast<const f32x4*>(lse_s[stage] + 32 * u + 8 * hh);
-        const f32x4* d4 = reinterpret_cast<const f32x4*>(dvec_s[stage] + 32 * u + 8 * hh);
-        const f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
-        const f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
+        // Register r of sub-tile u holds query row 32u + perm_row(r, hh).
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lv[r >> 2][r & 3]));
+        for (int uu = 0; uu < C::NG; ++uu) {
+          const f32x4* l4 = reinterpret_cast<const f32x4*>(lse_s[stage] + 32 * (g0 + uu) + 8 * hh);
+          const f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[uu][r] = __builtin_amdgcn_exp2f(fmaf(s[uu][r], sl2, -lv[r >> 2][r & 3]));
+        }
         if (need_mask) {
+          const bool kpad = my_k >= kvalid;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qi = q0b + 32 * u + perm_row(r, hh);
-            if ((p.causal && my_k > qi) || my_k >= kvalid) s[r] = 0.f;
-          }
+          for (int uu = 0; uu < C::NG; ++uu)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qi = q0b + 32 * (g0 + uu) + perm_row(r, hh);
+              const bool kill = (causal & (my_k > qi)) | kpad;  // branch-free select
+              s[uu][r] = kill ? 0.f : s[uu][r];
+            }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dv4[r >> 2][r & 3]);
+        for (int uu = 0; uu < C::NG; ++uu) {
+          const f32x4* d4 = reinterpret_cast<const f32x4*>(dvec_s[stage] + 32 * (g0 + uu) + 8 * hh);
+          const f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bf16x8 pf = pack8(s, c);
-          const bf16x8 dsf = pack8(dp, c);
-          const int rb = (32 * u + 16 * c) * T::RB;
+          for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * (dp[uu][r] - dv4[r >> 2][r & 3]);
 #pragma unroll
-          for (int db = 0; db < C::NDB; ++db) {
-            dvt[db] = mfma(lds_tr(dOs + rb, troff[db][0], troff[db][1]), pf, dvt[db]);
-            dkt[db] = mfma(lds_tr(Qs + rb, troff[db][0], troff[db][1]), dsf, dkt[db]);
+          for (int c = 0; c < 2; ++c) {
+            const bf16x8 pf = pack8(s[uu], c);
+            const bf16x8 dsf = pack8(dp[uu], c);
+            const int rb = (32 * (g0 + uu) + 16 * c) * T::RB;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+              dvt[db] = mfma(lds_tr(dOs + rb, troff[db][0], troff[db][1]), pf, dvt[db]);
+              dkt[db] = mfma(lds_tr(Qs + rb, troff[db][0], troff[db][1]), dsf, dkt[db]);
+            }
           }
         }
       }
@@ -303,6 +321,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int q0 = qb * C::BR;
   const int my_q = q0 + 32 * w + lr;
   const float sl2 = p.scale_l2;
+  const bool causal = p.causal != 0;
 
   const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;
   const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
@@ -368,8 +387,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const char* Vs = smem[stage] + T::BYTES;
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
-      const int sk0 = key0 + 32 * t;
-      if ((p.causal && sk0 > q0 + 32 * w + 31) || sk0 >= kvalid) continue;
       f32x16 st = f32x16{}, dpt = f32x16{};
       const char* kp = Ks + 32 * t * T::RB;
       const char* vp = Vs + 32 * t * T::RB;
@@ -392,8 +409,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = sk0 + perm_row(r, hh);
-          if ((p.causal && key > my_q) || key >= kvalid) st[r] = 0.f;
+          const int key = key0 + 32 * t + perm_row(r, hh);
+          const bool kill = (causal & (key > my_q)) | (key >= kvalid);  // branch-free select
+          st[r] = kill ? 0.f : st[r];
         }
       }
 #pragma unroll

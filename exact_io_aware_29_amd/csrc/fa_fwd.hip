@@ -107,12 +107,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
     if (need_mask) {
+      const bool causal = p.causal != 0;
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);
-          if ((p.causal && key > my_q) || key >= kvalid) s[t][r] = -kInf;
+          const bool kill = (causal & (key > my_q)) | (key >= kvalid);  // branch-free select
+          s[t][r] = kill ? -kInf : s[t][r];
         }
     }
 
@@ -320,12 +322,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
     if (need_mask) {
+      const bool causal = p.causal != 0;
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);
-          if ((p.causal && key > my_q) || key >= kvalid) s[t][r] = -kInf;
+          const bool kill = (causal & (key > my_q)) | (key >= kvalid);  // branch-free select
+          s[t][r] = kill ? -kInf : s[t][r];
         }
     }
     float mx = tree_max16(s[0]);
