@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 OBJDIR = os.path.join(ROOT, "_build")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+# Per-source extra flags. Matrix-core results go to VGPRs (the softmax reads
+# them directly, without v_accvgpr_read); the register allocator then uses
+# AGPRs as overflow for long-lived values.
+EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -35,7 +39,7 @@ FLAGS = [
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
           for (int r = 0; r < 16; ++r)
             s[uu][r] = __builtin_amdgcn_exp2f(fmaf(s[uu][r], sl2, -lv[r >> 2][r & 3]));
         }
-        if (need_mask) {
+        if (__builtin_expect(need_mask, false)) {  // boundary tiles only
           const bool kpad = my_k >= kvalid;
 #pragma unroll
           for (int uu = 0; uu < C::NG; ++uu)
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
-      if (need_mask) {
+      if (__builtin_expect(need_mask, false)) {  // boundary tiles only
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     }
 
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
-    if (need_mask) {
+    if (__builtin_expect(need_mask, false)) {  // boundary tiles only
       const bool causal = p.causal != 0;
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t)
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (need_mask) {
+    if (__builtin_expect(need_mask, false)) {  // boundary tiles only
       const bool causal = p.causal != 0;
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t)
