@@ -82,16 +82,21 @@ struct DkdvCfg {
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
   using T = SwzTile<D, BQ>;
+  // One stage: Q tile | dO tile | log2-domain LSE of its rows | D of its rows.
+  static constexpr int LSE_OFF = 2 * T::BYTES;
+  static constexpr int DVEC_OFF = LSE_OFF + 4 * BQ;
+  static constexpr int STAGE = DVEC_OFF + 4 * BQ;
 };
 
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<D>;
   using T = typename C::T;
-  // Two stages of (Q tile | dO tile), filled by DMA while the other is read.
-  __shared__ __attribute__((aligned(1024))) char smem[2][2 * T::BYTES];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][C::BQ];
-  __shared__ __attribute__((aligned(16))) float dvec_s[2][C::BQ];
+  // Two stages of (Q tile | dO tile | row statistics), filled while the
+  // other is read. One LDS object: every access goes through a stage pointer,
+  // so alias information can separate the stage being read from the one
+  // being filled.
+  __shared__ __attribute__((aligned(1024))) char smem[2][C::STAGE];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -148,48 +153,54 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     row_offsets<D, C::BQ>(roff, lr, hh);
     tr_offsets<D, C::BQ>(troff, lane);
 
+    // Row statistics of the next step are loaded with its DMA and used
+    // (converted, stored to LDS) only after the step's wait for that DMA, so
+    // that their first use does not stall on the tile loads issued before
+    // them.
     float lse_r = 0.f, dvec_r = 0.f;
-    auto issue = [&](int sidx, int stage) {
+    bool row_ok = false;
+    auto issue = [&](int sidx, char* stage) {
       const int h = hk * p.G + sidx / nq;
       const int q0b = (qfirst + sidx % nq) * C::BQ;
       const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
                                  (uint32_t)(p.N - 1) * qsb + 2 * D);
       const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
                                  (uint32_t)(p.N - 1) * dsb + 2 * D);
-      dma_tile<D, C::BQ>(qrs, qvo, (uint32_t)q0b * qsb, smem[stage], w);
-      dma_tile<D, C::BQ>(drs, dvo, (uint32_t)q0b * dsb, smem[stage] + T::BYTES, w);
+      dma_tile<D, C::BQ>(qrs, qvo, (uint32_t)q0b * qsb, stage, w);
+      dma_tile<D, C::BQ>(drs, dvo, (uint32_t)q0b * dsb, stage + T::BYTES, w);
       if (tid < C::BQ) {
         const int qi = q0b + tid;
-        const int64_t off = ((int64_t)b * p.Hq + h) * p.N + qi;
-        lse_r = qi < p.N ? lse2_of(a.lse[off]) : kInf;
-        dvec_r = qi < p.N ? a.dvec[off] : 0.f;
+        row_ok = qi < p.N;
+        const int64_t off = ((int64_t)b * p.Hq + h) * p.N + (row_ok ? qi : 0);
+        lse_r = a.lse[off];
+        dvec_r = a.dvec[off];
       }
     };
-    auto put_rowstats = [&](int stage) {
+    auto put_rowstats = [&](char* stage) {
       if (tid < C::BQ) {
-        lse_s[stage][tid] = lse_r;
-        dvec_s[stage][tid] = dvec_r;
+        reinterpret_cast<float*>(stage + C::LSE_OFF)[tid] = row_ok ? lse2_of(lse_r) : kInf;
+        reinterpret_cast<float*>(stage + C::DVEC_OFF)[tid] = row_ok ? dvec_r : 0.f;
       }
     };
 
     int sidx = next_step(0);
-    int stage = 0;
     if (sidx < nsteps) {
-      issue(sidx, 0);
-      put_rowstats(0);
+      issue(sidx, smem[0]);
       wait_dma();
+      put_rowstats(smem[0]);
       __syncthreads();
     }
-    while (sidx < nsteps) {
+    // One step reading stage `Qs` while the next lands in `fill`
+    // (restrict-qualified: these reads never wait for that DMA).
+    auto step = [&](const char* __restrict__ Qs, char* __restrict__ fill) {
+      const char* dOs = Qs + T::BYTES;
       const int h = hk * p.G + sidx / nq;
       const int q0b = (qfirst + sidx % nq) * C::BQ;
       const int nx = next_step(sidx + 1);
-      if (nx < nsteps) issue(nx, stage ^ 1);  // lands during this step
+      if (nx < nsteps) issue(nx, fill);  // lands during this step
       if (a.log_kv && tid == 0)
         log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
       const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid);
-      const char* Qs = smem[stage];
-      const char* dOs = smem[stage] + T::BYTES;
 
       // Straight-line step (no per-sub-tile branches): all S and dP products,
       // one uniform mask block, then P / dS and the dV, dK products, so the
@@ -222,7 +233,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         // Register r of sub-tile u holds query row 32u + perm_row(r, hh).
 #pragma unroll
         for (int uu = 0; uu < C::NG; ++uu) {
-          const f32x4* l4 = reinterpret_cast<const f32x4*>(lse_s[stage] + 32 * (g0 + uu) + 8 * hh);
+          const f32x4* l4 =
+              reinterpret_cast<const f32x4*>(Qs + C::LSE_OFF) + 8 * (g0 + uu) + 2 * hh;
           const f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
 #pragma unroll
           for (int r = 0; r < 16; ++r)
@@ -241,7 +253,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         }
 #pragma unroll
         for (int uu = 0; uu < C::NG; ++uu) {
-          const f32x4* d4 = reinterpret_cast<const f32x4*>(dvec_s[stage] + 32 * (g0 + uu) + 8 * hh);
+          const f32x4* d4 =
+              reinterpret_cast<const f32x4*>(Qs + C::DVEC_OFF) + 8 * (g0 + uu) + 2 * hh;
           const f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
 #pragma unroll
           for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * (dp[uu][r] - dv4[r >> 2][r & 3]);
@@ -259,13 +272,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
         }
       }
       if (nx < nsteps) {
-        put_rowstats(stage ^ 1);
         wait_dma();
+        put_rowstats(fill);
         __syncthreads();
       }
-      stage ^= 1;
       sidx = nx;
-    }
+    };
+    for (int st = 0; sidx < nsteps; st ^= 1) step(smem[st], smem[st ^ 1]);
   }
 
   if (my_k < p.N) {
@@ -365,26 +378,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
     return kt;
   };
-  auto issue = [&](int kt, int stage) {
-    dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, smem[stage], w);
-    dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, smem[stage] + T::BYTES, w);
+  auto issue = [&](int kt, char* stage) {
+    dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
+    dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
   };
 
   int kt = next_visit(0);
-  int stage = 0;
   if (kt < ntiles) {
-    issue(kt, 0);
+    issue(kt, smem[0]);
     wait_dma();
     __syncthreads();
   }
-  while (kt < ntiles) {
+  // One key tile read from stage `Ks` while the next lands in `fill`
+  // (restrict-qualified: these reads never wait for that DMA).
+  auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
+    const char* Vs = Ks + T::BYTES;
     const int key0 = kt * C::BC;
     const int nxt = next_visit(kt + 1);
-    if (nxt < ntiles) issue(nxt, stage ^ 1);
+    if (nxt < ntiles) issue(nxt, fill);
     if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
-    const char* Ks = smem[stage];
-    const char* Vs = smem[stage] + T::BYTES;
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
       f32x16 st = f32x16{}, dpt = f32x16{};
@@ -429,9 +442,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       wait_dma();
       __syncthreads();
     }
-    stage ^= 1;
     kt = nxt;
-  }
+  };
+  for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
 
   if (qok) {
     bf16* dqp = static_cast<bf16*>(a.dq) + b * a.sdq.b + h * a.sdq.h + (int64_t)my_q * a.sdq.n;

@@ -278,26 +278,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
     return kt;
   };
-  auto issue = [&](int kt, int st) {
-    dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, smem[st], w);
-    dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, smem[st] + T::BYTES, w);
+  auto issue = [&](int kt, char* stage) {
+    dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
+    dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
   };
 
   int kt = next_visit(0);
-  int st = 0;
   if (kt < ntiles) {
-    issue(kt, 0);
+    issue(kt, smem[0]);
     wait_dma();
     __syncthreads();
   }
-  while (kt < ntiles) {
+  // One key tile, read from stage `Ks` while the next visited tile lands in
+  // `fill`. The two restrict-qualified stages tell the compiler that these
+  // reads never alias that DMA, so it does not make the transposing reads
+  // wait for the DMA to land.
+  auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
+    const char* Vs = Ks + T::BYTES;
     const int key0 = kt * C::BC;
     const int nxt = next_visit(kt + 1);
-    if (nxt < ntiles) issue(nxt, st ^ 1);  // lands while this tile is computed
+    if (nxt < ntiles) issue(nxt, fill);  // lands while this tile is computed
     if (a.log && tid == 0) log_tile(a.log, log_row, key0);
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
-    const char* Ks = smem[st];
-    const char* Vs = smem[st] + T::BYTES;
 
     // One straight-line block per tile (no per-sub-tile branches), so the
     // compiler can overlap one sub-tile's exponentials with its neighbour's
@@ -367,9 +369,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
       wait_dma();
       __syncthreads();  // next tile landed everywhere; this tile is no longer read
     }
-    st ^= 1;
     kt = nxt;
-  }
+  };
+  for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
 
   const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
