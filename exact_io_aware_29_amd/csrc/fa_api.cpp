@@ -109,7 +109,7 @@ size_t fa_tile_log_words(const fa_params* p) {
 
 size_t fa_bwd_workspace_size(const fa_params* p) {
   if (check_params(p) != FA_OK) return 0;
-  return (size_t)p->batch * p->heads_q * p->seqlen * sizeof(float);
+  return 2 * (size_t)p->batch * p->heads_q * p->seqlen * sizeof(float);
 }
 
 int fa_fwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
@@ -192,6 +192,7 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   a.sdv = conv(sdv);
   a.lse = lse;
   a.dvec = static_cast<float*>(workspace);
+  a.lse2 = a.dvec + (size_t)p->batch * p->heads_q * p->seqlen;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

@@ -28,6 +28,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 // ----------------------------------------------------------------- D = rowsum(dO * O)
 
+// LSE in base-2 units; an empty row (LSE = -inf) becomes +inf so that every
+// rebuilt probability of that row is 2^-inf = 0.
+__device__ __forceinline__ float lse2_of(float lse) {
+  return lse == -kInf ? kInf : lse * kLog2e;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;  // lanes per row, 8 elements each
@@ -62,41 +68,52 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (part == 0 && row < rows) a.dvec[row] = acc;
+  if (part == 0 && row < rows) {
+    a.dvec[row] = acc;
+    a.lse2[row] = lse2_of(a.lse[row]);
+  }
 }
 
-// LSE in base-2 units; an empty row (LSE = -inf) becomes +inf so that every
-// rebuilt probability of that row is 2^-inf = 0.
-__device__ __forceinline__ float lse2_of(float lse) {
-  return lse == -kInf ? kInf : lse * kLog2e;
-}
 
 // ----------------------------------------------------------------- dK, dV
 
 template <int D>
 struct DkdvCfg {
-  static constexpr int BK = 128;       // keys per workgroup (4 waves x 32)
-  static constexpr int BQ = 8192 / D;  // query rows staged per step
+  static constexpr int BK = 128;  // keys per workgroup (4 waves x 32)
+  // At d=128 the dK and dV accumulators alone take 128 registers; the
+  // kernel keeps two waves per SIMD by staging 32 query rows per step (one
+  // sub-tile at a time) and reading V's operand fragments from an LDS copy of
+  // the workgroup's V block instead of holding them in registers.
+  static constexpr bool VLDS = D == 128;
+  static constexpr int BQ = D == 64 ? 128 : 32;  // query rows staged per step
   static constexpr int NQS = BQ / 32;
-  static constexpr int NG = 2;         // sub-tiles per straight-line group
+  static constexpr int NG = D == 64 ? 2 : 1;     // sub-tiles per straight-line group
+  static constexpr int FB = D == 64 ? 4 : 2;     // operand fragments fetched per batch
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
   using T = SwzTile<D, BQ>;
-  // One stage: Q tile | dO tile | log2-domain LSE of its rows | D of its rows.
+  using VT = SwzTile<D, BK>;
+  // One stage: Q tile | dO tile | log2-domain LSE of its rows | D of its
+  // rows. The row statistics arrive by dword DMA, 64 rows per wave load.
+  static constexpr int NRC = (BQ + 63) / 64;  // 64-row loads per statistic
   static constexpr int LSE_OFF = 2 * T::BYTES;
-  static constexpr int DVEC_OFF = LSE_OFF + 4 * BQ;
-  static constexpr int STAGE = DVEC_OFF + 4 * BQ;
+  static constexpr int DVEC_OFF = LSE_OFF + 256 * NRC;
+  static constexpr int STAGE = DVEC_OFF + 256 * NRC;
+  // LDS: two stages, then (VLDS) the V block of the workgroup's keys.
+  static constexpr int VOFF = 2 * STAGE;
+  static constexpr int LDS_BYTES = VOFF + (VLDS ? VT::BYTES : 0);
+  static_assert(STAGE % 256 == 0, "stages keep the 256-byte bank period");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<D>;
   using T = typename C::T;
   // Two stages of (Q tile | dO tile | row statistics), filled while the
-  // other is read. One LDS object: every access goes through a stage pointer,
-  // so alias information can separate the stage being read from the one
-  // being filled.
-  __shared__ __attribute__((aligned(1024))) char smem[2][C::STAGE];
+  // other is read, and at d=128 the V block. One LDS object: every access
+  // goes through a restrict-qualified pointer into it, so alias information
+  // can separate the stage being read from the one being filled.
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const Problem& p = a.p;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -115,15 +132,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
   const bf16* Kp = static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h;
   const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
 
-  // This lane's key as the B operand of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[C::NKK], vf[C::NKK];
+  // This lane's key as the B operand of S = Q K^T and dP = dO V^T (V from
+  // LDS at d=128).
+  bf16x8 kf[C::NKK], vf[C::VLDS ? 1 : C::NKK];
   {
     const bool ok = my_k < p.N;
     const int64_t r = ok ? my_k : 0;
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) {
       kf[kk] = frag_g(Kp + r * a.sk.n + 16 * kk + 8 * hh, ok);
-      vf[kk] = frag_g(Vp + r * a.sv.n + 16 * kk + 8 * hh, ok);
+      if constexpr (!C::VLDS) vf[kk] = frag_g(Vp + r * a.sv.n + 16 * kk + 8 * hh, ok);
     }
   }
 
@@ -147,18 +165,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
     };
     const int qsb = 2 * (int)a.sq.n, dsb = 2 * (int)a.sdo.n;
     int qvo[T::NLD], dvo[T::NLD];
-    dma_offsets<D, C::BQ>(qvo, qsb, w, lane);
-    dma_offsets<D, C::BQ>(dvo, dsb, w, lane);
+    if constexpr (!C::VLDS) {
+      dma_offsets<D, C::BQ>(qvo, qsb, w, lane);
+      dma_offsets<D, C::BQ>(dvo, dsb, w, lane);
+    }
+    static_assert(2 * C::NRC <= 4, "one wave per 64-row statistics load");
     int roff[C::NKK], troff[C::NDB][2];
     row_offsets<D, C::BQ>(roff, lr, hh);
     tr_offsets<D, C::BQ>(troff, lane);
 
-    // Row statistics of the next step are loaded with its DMA and used
-    // (converted, stored to LDS) only after the step's wait for that DMA, so
-    // that their first use does not stall on the tile loads issued before
-    // them.
-    float lse_r = 0.f, dvec_r = 0.f;
-    bool row_ok = false;
+    // Q and dO tiles of a step and the LSE / D values of its rows all arrive
+    // by DMA into the stage; rows past the sequence read as zero, and with
+    // their Q and dO rows zero they add nothing to dK or dV.
     auto issue = [&](int sidx, char* stage) {
       const int h = hk * p.G + sidx / nq;
       const int q0b = (qfirst + sidx % nq) * C::BQ;
@@ -166,33 +184,49 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
                                  (uint32_t)(p.N - 1) * qsb + 2 * D);
       const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
                                  (uint32_t)(p.N - 1) * dsb + 2 * D);
+      if constexpr (C::VLDS) {
+        // Registers are at their limit here: rebuild the DMA offsets for
+        // this step from the lane index (laundered so that they are not
+        // hoisted out of the loop and kept live).
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        dma_offsets<D, C::BQ>(qvo, qsb, w, ln);
+        dma_offsets<D, C::BQ>(dvo, dsb, w, ln);
+      }
       dma_tile<D, C::BQ>(qrs, qvo, (uint32_t)q0b * qsb, stage, w);
       dma_tile<D, C::BQ>(drs, dvo, (uint32_t)q0b * dsb, stage + T::BYTES, w);
-      if (tid < C::BQ) {
-        const int qi = q0b + tid;
-        row_ok = qi < p.N;
-        const int64_t off = ((int64_t)b * p.Hq + h) * p.N + (row_ok ? qi : 0);
-        lse_r = a.lse[off];
-        dvec_r = a.dvec[off];
-      }
-    };
-    auto put_rowstats = [&](char* stage) {
-      if (tid < C::BQ) {
-        reinterpret_cast<float*>(stage + C::LSE_OFF)[tid] = row_ok ? lse2_of(lse_r) : kInf;
-        reinterpret_cast<float*>(stage + C::DVEC_OFF)[tid] = row_ok ? dvec_r : 0.f;
+      if (w < 2 * C::NRC) {  // wave-uniform: one 64-row load of LSE or D
+        const int64_t row0 = ((int64_t)b * p.Hq + h) * p.N;
+        const bool is_d = w >= C::NRC;
+        const int c = is_d ? w - C::NRC : w;
+        const Rsrc rs = make_rsrc((is_d ? a.dvec : a.lse2) + row0, (uint32_t)p.N * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (FA_LDS void*)(stage + (is_d ? C::DVEC_OFF : C::LSE_OFF) + 256 * c), 4, 4 * lane,
+            (uint32_t)(q0b + 64 * c) * 4, 0, 0);
       }
     };
 
-    int sidx = next_step(0);
-    if (sidx < nsteps) {
-      issue(sidx, smem[0]);
-      wait_dma();
-      put_rowstats(smem[0]);
-      __syncthreads();
+    // B-operand offsets of this lane's key row in the V block.
+    int vboff[C::VLDS ? C::NKK : 1];
+    if constexpr (C::VLDS) {
+      using VT = typename C::VT;
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) vboff[kk] = VT::off(32 * w + lr, 2 * kk + hh);
+      int vvo[VT::NLD];
+      const int vsb = 2 * (int)a.sv.n;
+      dma_offsets<D, C::BK>(vvo, vsb, w, lane);
+      const Rsrc vrs = make_rsrc(Vp, (uint32_t)(p.N - 1) * vsb + 2 * D);
+      dma_tile<D, C::BK>(vrs, vvo, (uint32_t)k0 * vsb, smem + C::VOFF, w);
     }
+
+    int sidx = next_step(0);
+    if (sidx < nsteps) issue(sidx, smem);
+    wait_dma();  // the V block (if staged) and the first step
+    __syncthreads();
     // One step reading stage `Qs` while the next lands in `fill`
     // (restrict-qualified: these reads never wait for that DMA).
-    auto step = [&](const char* __restrict__ Qs, char* __restrict__ fill) {
+    auto step = [&](const char* __restrict__ Qs, char* __restrict__ fill,
+                    const char* __restrict__ Vb) {
       const char* dOs = Qs + T::BYTES;
       const int h = hk * p.G + sidx / nq;
       const int q0b = (qfirst + sidx % nq) * C::BQ;
@@ -216,17 +250,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
           const char* qp = Qs + 32 * (g0 + uu) * T::RB;
           const char* dop = dOs + 32 * (g0 + uu) * T::RB;
 #pragma unroll
-          for (int k4 = 0; k4 < C::NKK; k4 += 4) {
-            bf16x8 qa[4], da[4];
+          for (int k4 = 0; k4 < C::NKK; k4 += C::FB) {
+            bf16x8 qa[C::FB], da[C::FB], va[C::FB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < C::FB; ++i) {
               qa[i] = lds_row(qp, roff[k4 + i]);
               da[i] = lds_row(dop, roff[k4 + i]);
+              if constexpr (C::VLDS) va[i] = lds_row(Vb, vboff[k4 + i]);
+              else va[i] = vf[k4 + i];
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < C::FB; ++i) {
               s[uu] = mfma(qa[i], kf[k4 + i], s[uu]);
-              dp[uu] = mfma(da[i], vf[k4 + i], dp[uu]);
+              dp[uu] = mfma(da[i], va[i], dp[uu]);
             }
           }
         }
@@ -273,12 +309,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs 
       }
       if (nx < nsteps) {
         wait_dma();
-        put_rowstats(fill);
         __syncthreads();
       }
       sidx = nx;
     };
-    for (int st = 0; sidx < nsteps; st ^= 1) step(smem[st], smem[st ^ 1]);
+    for (int st = 0; sidx < nsteps; st ^= 1)
+      step(smem + st * C::STAGE, smem + (st ^ 1) * C::STAGE, smem + C::VOFF);
   }
 
   if (my_k < p.N) {
@@ -355,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
   const int64_t rowstat = ((int64_t)b * p.Hq + h) * p.N + (qok ? my_q : 0);
-  const float lse2 = qok ? lse2_of(a.lse[rowstat]) : kInf;
+  const float lse2 = qok ? a.lse2[rowstat] : kInf;
   const float dq_d = qok ? a.dvec[rowstat] : 0.f;
 
   int kvo[T::NLD], vvo[T::NLD];

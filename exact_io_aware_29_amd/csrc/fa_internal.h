@@ -45,6 +45,7 @@ struct BwdArgs {
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   const float* lse;
   float* dvec;  // workspace: D = rowsum(dO * O), fp32 [B][Hq][N]
+  float* lse2;  // workspace: LSE * log2(e) (+inf for empty rows), fp32 [B][Hq][N]
   void* dq;
   void* dk;
   void* dv;

@@ -157,26 +157,28 @@ struct SwzTile {
 };
 
 // Per-lane global byte offsets (relative to the tile's first row) of the
-// DMA loads that fill one tile; computed once per kernel.
-template <int D, int ROWS, int NL>
+// DMA loads that fill one tile when NW waves share the work; computed once
+// per kernel. Wave w's load i fills LDS kibibyte i * NW + w of the tile.
+template <int D, int ROWS, int NL, int NW = 4>
 __device__ __forceinline__ void dma_offsets(int (&voff)[NL], int stride_bytes, int w, int lane) {
   using T = SwzTile<D, ROWS>;
-  static_assert(NL == T::NLD, "one offset per DMA load");
+  static_assert(NL * NW * 1024 == T::BYTES, "one offset per DMA load");
 #pragma unroll
-  for (int i = 0; i < T::NLD; ++i) {
-    const int p = (i * 4 + w) * 64 + lane;  // 16-byte LDS position
+  for (int i = 0; i < NL; ++i) {
+    const int p = (i * NW + w) * 64 + lane;  // 16-byte LDS position
     const int r = p / T::CPR, pc = p % T::CPR;
     voff[i] = r * stride_bytes + 16 * (pc ^ T::swz(r));
   }
 }
 
-template <int D, int ROWS>
+template <int D, int ROWS, int NW = 4>
 __device__ __forceinline__ void dma_tile(Rsrc rs, const int* voff, uint32_t soff, char* tile,
                                          int w) {
   using T = SwzTile<D, ROWS>;
+  constexpr int NL = T::BYTES / (NW * 1024);
 #pragma unroll
-  for (int i = 0; i < T::NLD; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + (i * 4 + w) * 1024), 16,
+  for (int i = 0; i < NL; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + (i * NW + w) * 1024), 16,
                                              voff[i], soff, 0, 0);
 }
 

@@ -137,13 +137,15 @@ int fa_fwd(const fa_params* p,
 /* Number of uint32 words of one tile log (fa_fwd); fa_bwd takes twice this. */
 size_t fa_tile_log_words(const fa_params* p);
 
-/* Bytes of device workspace fa_bwd needs (the row vector D, fp32 [B][Hq][N]). */
+/* Bytes of device workspace fa_bwd needs: two fp32 [B][Hq][N] row vectors,
+ * D and the log-sum-exp in base-2 units. */
 size_t fa_bwd_workspace_size(const fa_params* p);
 
 /*
  * fa_bwd -- recomputation backward (the report's sections 2.5 and 3.3; the
  * tutorial's backward paragraph). Three kernels run in order on `stream`:
- *   1. D_i = sum_t dO[i][t] * O[i][t] into the workspace (fp32);
+ *   1. D_i = sum_t dO[i][t] * O[i][t] and LSE_i * log2(e) into the
+ *      workspace (fp32; +inf for a row with no allowed key);
  *   2. per block of 128 keys of one key/value head: for every query head of
  *      its group and every visited query tile, rebuild
  *      P = exp(scale * q.k - LSE), dP = dO V^T, dS = P * (dP - D) and

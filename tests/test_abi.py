@@ -128,7 +128,7 @@ def test_bwd_validation():
     p = _params()
     s, skv = _strides(p), _strides(p, p.heads_kv)
     need = fa.fa_bwd_workspace_size(p)
-    assert need == 2 * 4 * 300 * 4
+    assert need == 2 * (2 * 4 * 300) * 4  # D and the base-2 LSE
 
     def call(p=p, ws=ctypes.c_void_p(0x7000), nbytes=need, ev=None):
         return lib.fa_bwd(ctypes.byref(p), P16, s, P32, skv, P48, skv, P64, s, P80, s,
@@ -149,6 +149,7 @@ def test_size_queries():
     p = _params(seqlen=4097)
     nlb = 33
     assert fa.fa_tile_log_words(p) == 2 * 4 * nlb * 2
-    assert fa.fa_bwd_workspace_size(p) == 2 * 4 * 4097 * 4
+    # two fp32 row vectors (D and the base-2 LSE) of B * Hq * N entries
+    assert fa.fa_bwd_workspace_size(p) == 2 * (2 * 4 * 4097) * 4
     assert fa.fa_tile_log_words(_params(head_dim=80)) == 0
     assert fa.fa_bwd_workspace_size(_params(heads_q=3)) == 0
