@@ -310,17 +310,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     // sharing the SIMD fill the VALU between its products.
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int t = 0; t < C::NSUB; ++t) {
-      s[t] = f32x16{};
-      const char* kp = Ks + 32 * t * T::RB;
+    for (int t = 0; t < C::NSUB; ++t) s[t] = f32x16{};
+    // Head-dim steps outer, sub-tiles inner: the sub-tiles' accumulation
+    // chains interleave.
 #pragma unroll
-      for (int k4 = 0; k4 < C::NKK; k4 += 4) {
-        bf16x8 ka[4];
+    for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ka[i] = lds_row(kp, roff[k4 + i]);
+      for (int t = 0; t < C::NSUB; ++t)
+        s[t] = mfma(lds_row(Ks + 32 * t * T::RB, roff[kk]), qf[kk], s[t]);
+    {
+      // Keep four operand fragments in flight ahead of the products.
+      constexpr int NM = C::NSUB * C::NKK;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[t] = mfma(ka[i], qf[k4 + i], s[t]);
+      for (int i = 0; i < NM - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     __builtin_amdgcn_s_setprio(0);
     if (__builtin_expect(need_mask, false)) {  // boundary tiles only
@@ -362,6 +369,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
           acc[db] = mfma(lds_tr(vp, troff[db][0], troff[db][1]), pf, acc[db]);
+      }
+      {
+        // Transposing reads of four operands in flight ahead of the products.
+        constexpr int NM = 2 * C::NDB;
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < NM - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       __builtin_amdgcn_s_setprio(0);
     }
