@@ -39,14 +39,20 @@ Masks (all boolean, combined with AND):
   computed and still attend to the first min(i + 1, L_b) keys under causal);
 * block mask BM of granularity ``mask_block``: allowed iff
   BM[i // mask_block][j // mask_block] != 0 (the block-sparse variant of the
-  report, section 2.6 / section 3.5).
+  report, section 2.6 / section 3.5);
+* sliding window (left, right): allowed iff i - left <= j <= i + right.
+  The pages name the sliding window only as an attention variant (the
+  synthesis page, section 5 item 1) and as one of the sparse patterns that
+  skip blocks of the score matrix (the tutorial page, "sparse attention");
+  this two-sided band is the plain reading (right = 0 with causal is the
+  usual causal local attention).
 
 Everything is float64; inputs are the exact values the GPU sees, widened.
 """
 from __future__ import annotations
 
 import dataclasses
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -61,6 +67,7 @@ class MaskSpec:
     seqlen_k: Optional[int] = None  # valid key count L_b, or None for all
     block_mask: Optional[np.ndarray] = None  # [nqb, nkb] 0/1
     mask_block: int = 128
+    window: Optional[Tuple[int, int]] = None  # (left, right) band, or None
 
     def allowed(self, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
         """Boolean [len(rows), len(cols)]: may query ``rows[a]`` see key ``cols[c]``."""
@@ -74,14 +81,18 @@ class MaskSpec:
         if self.block_mask is not None:
             bm = np.asarray(self.block_mask) != 0
             ok &= bm[i // self.mask_block, j // self.mask_block]
+        if self.window is not None:
+            left, right = self.window
+            ok &= (j >= i - left) & (j <= i + right)
         return ok
 
 
 def mask_for(b: int, *, causal=False, seqlens=None, block_mask=None,
-             mask_block=128) -> MaskSpec:
+             mask_block=128, window=None) -> MaskSpec:
     """MaskSpec of batch entry ``b`` from whole-problem mask arguments."""
     L = None if seqlens is None else int(np.asarray(seqlens)[b])
-    return MaskSpec(bool(causal), L, block_mask, mask_block)
+    win = None if window is None else (int(window[0]), int(window[1]))
+    return MaskSpec(bool(causal), L, block_mask, mask_block, win)
 
 
 def _softmax_rows(s: np.ndarray):
@@ -187,7 +198,7 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
 
 
 def attention_forward(q, k, v, scale, *, causal=False, seqlens=None,
-                      block_mask=None, mask_block=128):
+                      block_mask=None, mask_block=128, window=None):
     """Whole-tensor forward. q: [B, Hq, N, d], k/v: [B, Hkv, N, d] (float64).
 
     Returns O [B, Hq, N, d] and LSE [B, Hq, N].
@@ -198,7 +209,7 @@ def attention_forward(q, k, v, scale, *, causal=False, seqlens=None,
     lse = np.zeros((B, Hq, N))
     for b in range(B):
         m = mask_for(b, causal=causal, seqlens=seqlens, block_mask=block_mask,
-                     mask_block=mask_block)
+                     mask_block=mask_block, window=window)
         for h in range(Hq):
             o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h // G], v[b, h // G],
                                               scale, m)
@@ -206,7 +217,7 @@ def attention_forward(q, k, v, scale, *, causal=False, seqlens=None,
 
 
 def attention_backward(q, k, v, do, scale, *, causal=False, seqlens=None,
-                       block_mask=None, mask_block=128):
+                       block_mask=None, mask_block=128, window=None):
     """Whole-tensor backward. Returns dQ [B,Hq,N,d], dK, dV [B,Hkv,N,d]."""
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -216,7 +227,7 @@ def attention_backward(q, k, v, do, scale, *, causal=False, seqlens=None,
     dv = np.zeros(v.shape)
     for b in range(B):
         m = mask_for(b, causal=causal, seqlens=seqlens, block_mask=block_mask,
-                     mask_block=mask_block)
+                     mask_block=mask_block, window=window)
         for h in range(Hq):
             g = h // G
             a, bk, bv = head_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, m)

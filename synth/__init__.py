@@ -47,6 +47,7 @@ class Workload:
     pad_range: Optional[tuple] = None  # inclusive (lo, hi) for key lengths
     butterfly: bool = False
     backward: bool = True
+    window: Optional[tuple] = None  # (left, right) sliding-window band
 
     @property
     def group(self) -> int:
@@ -71,6 +72,8 @@ class Workload:
             parts.append(f"keypad{self.pad_range[0]}-{self.pad_range[1]}")
         if self.butterfly:
             parts.append("butterfly128")
+        if self.window is not None:
+            parts.append(f"window{self.window[0]}-{self.window[1]}")
         parts.append("fwd+bwd" if self.backward else "fwd")
         return " ".join(parts)
 
@@ -83,6 +86,10 @@ WORKLOADS = {
                 pad_range=(2048, 4096)),
     4: Workload("long-causal-gqa", 1, 32, 8, 16384, 128, "bf16", causal=True),
     5: Workload("butterfly-64k", 1, 8, 8, 65536, 64, "bf16", butterfly=True),
+    # Causal local attention: each query sees itself and the 1023 keys before
+    # it (a sliding window; no such shape is fixed by the pages).
+    6: Workload("sliding-window-8k", 4, 16, 16, 8192, 128, "bf16", causal=True,
+                window=(1023, 0)),
 }
 
 
@@ -129,6 +136,7 @@ class Inputs:
     seqlens: Optional[np.ndarray]
     block_mask: Optional[np.ndarray]
     scale: float
+    window: Optional[tuple] = None
 
     def as_f64(self, name: str, index=None) -> np.ndarray:
         """Exact float64 view of tensor ``name`` (optionally sliced first)."""
@@ -163,12 +171,12 @@ def draw(w: Workload, seed: int, *, with_do: Optional[bool] = None) -> Inputs:
     if w.butterfly:
         nb = -(-w.seqlen // MASK_BLOCK)
         block_mask = butterfly_block_mask(nb)
-    return Inputs(w, q, k, v, do, seqlens, block_mask, w.scale)
+    return Inputs(w, q, k, v, do, seqlens, block_mask, w.scale, w.window)
 
 
 def draw_case(batch, heads_q, heads_kv, seqlen, head_dim, dtype="bf16", *,
               causal=False, seqlens=None, block_mask=None, seed=0,
-              with_do=True) -> Inputs:
+              with_do=True, window=None) -> Inputs:
     """Draw an ad-hoc problem (used by the small parity cases).
 
     ``seqlens`` may be None, a sequence of ints, or "random" (uniform over
@@ -196,4 +204,5 @@ def draw_case(batch, heads_q, heads_kv, seqlen, head_dim, dtype="bf16", *,
             raise ValueError(block_mask)
     if block_mask is not None:
         inp.block_mask = np.ascontiguousarray(block_mask, dtype=np.uint8)
+    inp.window = None if window is None else (int(window[0]), int(window[1]))
     return inp

@@ -4,14 +4,20 @@ Used only to pin the vectorised oracle. Nothing here uses numpy's matmul or
 exp: each score is a Python sum of products, each exponential math.exp, and
 the mask is re-derived from its plain-language rules:
 causal (key index <= query index), key padding (key index < valid length),
-block mask (the block of (query, key) is present).
+block mask (the block of (query, key) is present), sliding window (the key
+is at most `left` positions before and `right` positions after the query).
 """
 import math
 
 
-def allowed(i, j, causal=False, seqlen_k=None, block_mask=None, mask_block=128):
+def allowed(i, j, causal=False, seqlen_k=None, block_mask=None, mask_block=128,
+            window=None):
     if causal and j > i:
         return False
+    if window is not None:
+        left, right = window
+        if i - j > left or j - i > right:
+            return False
     if seqlen_k is not None and j >= seqlen_k:
         return False
     if block_mask is not None and not block_mask[i // mask_block][j // mask_block]:

@@ -29,12 +29,16 @@ MASKS = [
     dict(causal=True, seqlen_k=6),
     dict(block_mask=np.array([[1, 0, 1], [0, 1, 0], [1, 1, 1]]), mask_block=4),
     dict(causal=True, block_mask=np.array([[1, 0, 1], [1, 1, 0], [1, 1, 1]]), mask_block=4),
+    dict(window=(2, 1)),
+    dict(causal=True, window=(3, 0)),
+    dict(seqlen_k=7, window=(1, 4)),
 ]
+WINDOW_MASK = 6  # index of the first sliding-window entry
 
 
 def _spec(m):
     return OA.MaskSpec(m.get("causal", False), m.get("seqlen_k"), m.get("block_mask"),
-                       m.get("mask_block", 128))
+                       m.get("mask_block", 128), m.get("window"))
 
 
 # ---------------------------------------------------------------- forward pins
@@ -120,6 +124,35 @@ def test_zero_query_closed_forms_named_cases():
     L = 37
     o, lse = OA.head_forward(z, rand(n, d), v, 1.0, OA.MaskSpec(causal=True, seqlen_k=L))
     np.testing.assert_allclose(lse, np.log(np.minimum(np.arange(1, n + 1), L)), atol=1e-14)
+    # sliding window (l, r): count = min(i, l) + min(n - 1 - i, r) + 1, and the
+    # output is the mean of V over the band
+    l, r = 5, 2
+    o, lse = OA.head_forward(z, rand(n, d), v, 1.0, OA.MaskSpec(window=(l, r)))
+    i = np.arange(n)
+    cnt = np.minimum(i, l) + np.minimum(n - 1 - i, r) + 1
+    np.testing.assert_allclose(lse, np.log(cnt), atol=1e-14)
+    band = np.array([v[max(0, t - l):min(n, t + r + 1)].mean(axis=0) for t in range(n)])
+    np.testing.assert_allclose(o, band, atol=1e-14)
+
+
+def test_window_of_width_zero_is_the_diagonal():
+    """Window (0, 0): each row sees only its own key, so O_i = V_i and
+    LSE_i = scale * q_i . k_i exactly (a one-term softmax)."""
+    n, d = 20, 7
+    q, k, v = rand(n, d), rand(n, d), rand(n, d)
+    o, lse = OA.head_forward(q, k, v, 0.6, OA.MaskSpec(window=(0, 0)))
+    np.testing.assert_allclose(o, v, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.6 * (q * k).sum(axis=1), atol=1e-14)
+
+
+def test_window_covering_everything_is_no_window():
+    n, d = 24, 5
+    q, k, v = rand(n, d), rand(n, d), rand(n, d)
+    for causal in (False, True):
+        o1, l1 = OA.head_forward(q, k, v, 0.4, OA.MaskSpec(causal=causal))
+        o2, l2 = OA.head_forward(q, k, v, 0.4, OA.MaskSpec(causal=causal, window=(n, n)))
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
 
 
 def _partial(q, k, v, scale, cols):
@@ -270,6 +303,8 @@ FD_CASES = [
     dict(seqlens=np.array([5])),
     dict(causal=True, seqlens=np.array([4])),
     dict(block_mask=np.array([[1, 0], [1, 1]]), mask_block=4),
+    dict(window=(2, 1)),
+    dict(causal=True, window=(2, 0)),
 ]
 
 
@@ -336,6 +371,7 @@ def _pins_pass():
         test_brute_force_forward(1)
         test_brute_force_forward(2)
         test_brute_force_forward(4)
+        test_brute_force_forward(WINDOW_MASK)
         test_zero_query_closed_forms_named_cases()
         test_gqa_equals_repeated_mha()
         test_finite_difference_gradients(1, 2)
@@ -373,12 +409,31 @@ def _mut_lse_without_max(s):
     return p, np.where(np.isfinite(lse), lse - m, lse)
 
 
+def _mut_window_swapped(self, rows, cols):
+    """Sliding window with its left and right widths exchanged."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.asarray(cols, dtype=np.int64)[None, :]
+    ok = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+    if self.causal:
+        ok &= j <= i
+    if self.seqlen_k is not None:
+        ok &= j < self.seqlen_k
+    if self.block_mask is not None:
+        ok &= np.asarray(self.block_mask)[i // self.mask_block, j // self.mask_block] != 0
+    if self.window is not None:
+        right, left = self.window
+        ok &= (j >= i - left) & (j <= i + right)
+    return ok
+
+
 @pytest.mark.parametrize("mutant", ["causal", "scale", "lse", "dq_scale", "ds_no_d",
-                                    "gqa_index"])
+                                    "gqa_index", "window_swapped"])
 def test_mutants_are_caught(mutant, monkeypatch):
     assert _pins_pass()  # sanity: the real oracle passes
     if mutant == "causal":
         monkeypatch.setattr(OA.MaskSpec, "allowed", _mut_causal_flipped)
+    elif mutant == "window_swapped":
+        monkeypatch.setattr(OA.MaskSpec, "allowed", _mut_window_swapped)
     elif mutant == "scale":
         monkeypatch.setattr(OA, "_scores", _mut_no_scale)
     elif mutant == "lse":
