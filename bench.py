@@ -88,7 +88,8 @@ def cpu_baseline(inp, pairs_per_head, budget_s):
     done, flop = 0, 0
     t0 = time.perf_counter()
     for b in range(w.batch):
-        m = mask_for(b, causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask)
+        m = mask_for(b, causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask,
+                     window=w.window)
         for h in range(w.heads_q):
             q = inp.as_f64("q", (b, h))
             k = inp.as_f64("k", (b, h // G))
@@ -142,7 +143,7 @@ def main():
     do = t(inp.do) if w.backward else None
     sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).to(dev)
     bm = None if inp.block_mask is None else torch.from_numpy(inp.block_mask).to(dev)
-    kw = dict(scale=inp.scale, causal=w.causal, seqlens_k=sl, block_mask=bm)
+    kw = dict(scale=inp.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, window=w.window)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     if w.backward:
@@ -194,7 +195,7 @@ def main():
 
     per_b = [int(acc.allowed_pairs_per_row(
         w.seqlen, causal=w.causal, seqlen_k=None if inp.seqlens is None else int(inp.seqlens[b]),
-        block_mask=inp.block_mask).sum()) for b in range(w.batch)]
+        block_mask=inp.block_mask, window=w.window).sum()) for b in range(w.batch)]
     pairs = sum(per_b) * w.heads_q
     fl = acc.flops(pairs, w.head_dim)
     ms_step = wall / args.steps * 1e3

@@ -55,14 +55,18 @@ def _strides(t: torch.Tensor) -> Strides:
 
 
 def make_params(*, dtype=FA_BF16, o_dtype=None, batch, heads_q, heads_kv, seqlen, head_dim,
-                scale=None, causal=False, seqlens_k=0, block_mask=0, block_mask_ld=0) -> Params:
-    """fa_params from plain values (device pointers as ints)."""
+                scale=None, causal=False, seqlens_k=0, block_mask=0, block_mask_ld=0,
+                window=None) -> Params:
+    """fa_params from plain values (device pointers as ints); ``window`` is
+    None or a (left, right) sliding-window band."""
+    wl, wr = (0, 0) if window is None else (int(window[0]), int(window[1]))
     return Params(dtype, dtype if o_dtype is None else o_dtype, batch, heads_q, heads_kv, seqlen,
                   head_dim, 1.0 / math.sqrt(head_dim) if scale is None else scale, int(bool(causal)),
-                  seqlens_k or None, block_mask or None, block_mask_ld)
+                  seqlens_k or None, block_mask or None, block_mask_ld,
+                  int(window is not None), wl, wr)
 
 
-def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype) -> Params:
+def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype, window) -> Params:
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if k.dtype != q.dtype:
@@ -85,7 +89,7 @@ def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype) -> Para
     odt = _DT[q.dtype] if o_dtype is None else _DT[o_dtype]
     return make_params(dtype=_DT[q.dtype], o_dtype=odt, batch=B, heads_q=Hq, heads_kv=k.shape[1],
                        seqlen=N, head_dim=d, scale=scale, causal=causal, seqlens_k=sl_ptr,
-                       block_mask=bm_ptr, block_mask_ld=bm_ld)
+                       block_mask=bm_ptr, block_mask_ld=bm_ld, window=window)
 
 
 def _stream() -> ctypes.c_void_p:
@@ -108,11 +112,11 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
            causal: bool = False, seqlens_k: Optional[torch.Tensor] = None,
            block_mask: Optional[torch.Tensor] = None, o_dtype: Optional[torch.dtype] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           tile_log: bool = False):
+           tile_log: bool = False, window: Optional[tuple] = None):
     """Forward pass. Returns (O, LSE, tile_log or None)."""
     lib = _abi.load()
     p = _params_from(q, k, scale=scale, causal=causal, seqlens_k=seqlens_k,
-                     block_mask=block_mask, o_dtype=o_dtype)
+                     block_mask=block_mask, o_dtype=o_dtype, window=window)
     B, Hq, N, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=o_dtype or q.dtype, device=q.device)
@@ -136,7 +140,8 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
            seqlens_k: Optional[torch.Tensor] = None, block_mask: Optional[torch.Tensor] = None,
            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
            dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-           tile_log: bool = False, stage_events: Optional[Sequence] = None):
+           tile_log: bool = False, stage_events: Optional[Sequence] = None,
+           window: Optional[tuple] = None):
     """Backward pass. Returns (dQ, dK, dV, tile_log or None).
 
     ``stage_events``: optional 4 ``torch.cuda.Event`` objects, recorded by
@@ -144,7 +149,7 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
     """
     lib = _abi.load()
     p = _params_from(q, k, scale=scale, causal=causal, seqlens_k=seqlens_k,
-                     block_mask=block_mask, o_dtype=o.dtype)
+                     block_mask=block_mask, o_dtype=o.dtype, window=window)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

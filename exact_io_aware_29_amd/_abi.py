@@ -45,6 +45,9 @@ class Params(ctypes.Structure):
         ("seqlens_k", ctypes.c_void_p),
         ("block_mask", ctypes.c_void_p),
         ("block_mask_ld", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 

@@ -37,50 +37,78 @@ HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
 
 
 def allowed_pairs_per_row(N: int, *, causal=False, seqlen_k: Optional[int] = None,
-                          block_mask: Optional[np.ndarray] = None, block=128) -> np.ndarray:
-    """int64 [N]: number of allowed keys of each query row of one sequence."""
+                          block_mask: Optional[np.ndarray] = None, block=128,
+                          window=None) -> np.ndarray:
+    """int64 [N]: number of allowed keys of each query row of one sequence.
+
+    Row i's allowed keys (before the block mask) are the interval
+    [lo_i, cap_i): lo_i = max(0, i - left) under a (left, right) window, and
+    cap_i the least of L, i + 1 (causal) and i + right + 1 (window)."""
     i = np.arange(N, dtype=np.int64)
     L = N if seqlen_k is None else int(min(max(seqlen_k, 0), N))
     cap = np.minimum(i + 1, L) if causal else np.full(N, L, dtype=np.int64)
+    lo = np.zeros(N, dtype=np.int64)
+    if window is not None:
+        cap = np.minimum(cap, i + int(window[1]) + 1)
+        lo = np.maximum(0, i - int(window[0]))
     if block_mask is None:
-        return cap
+        return np.clip(cap - lo, 0, None)
     nb = -(-N // block)
     bm = np.asarray(block_mask)[:nb, :nb] != 0
     out = np.zeros(N, dtype=np.int64)
     for kb in range(nb):
-        lo = kb * block
-        hi = min(N, lo + block)
+        k0 = kb * block
+        k1 = min(N, k0 + block)
         rows_on = bm[i // block, kb]
-        cnt = np.clip(np.minimum(cap, hi) - lo, 0, None)
+        cnt = np.clip(np.minimum(cap, k1) - np.maximum(lo, k0), 0, None)
         out += np.where(rows_on, cnt, 0)
     return out
 
 
-def allowed_pairs(B: int, Hq: int, N: int, *, causal=False, seqlens=None, block_mask=None) -> int:
+def allowed_pairs(B: int, Hq: int, N: int, *, causal=False, seqlens=None, block_mask=None,
+                  window=None) -> int:
     """Total allowed (query, key) pairs over all batches and query heads."""
     total = 0
     for b in range(B):
         L = None if seqlens is None else int(seqlens[b])
         total += int(allowed_pairs_per_row(N, causal=causal, seqlen_k=L,
-                                           block_mask=block_mask).sum())
+                                           block_mask=block_mask, window=window).sum())
     return total * Hq
 
 
-def visited_tiles(B: int, Hq: int, N: int, *, causal=False, seqlens=None, block_mask=None,
-                  block=128) -> int:
-    """Number of 128 x 128 tiles with at least one allowed pair."""
+def tile_map(N: int, *, causal=False, seqlen_k: Optional[int] = None, block_mask=None,
+             block=128, window=None) -> np.ndarray:
+    """bool [nb, nb]: which block x block tiles of one sequence hold an
+    allowed pair. Over the rows r0..r1 of a row block, the allowed keys
+    (before the block mask) form one interval: from r0 - left to the least
+    of L - 1, r1 (causal) and r1 + right."""
     nb = -(-N // block)
-    qb = np.arange(nb)[:, None]
-    kb = np.arange(nb)[None, :]
+    r0 = np.arange(nb)[:, None] * block
+    r1 = np.minimum(r0 + block, N) - 1
+    c0 = np.arange(nb)[None, :] * block
+    c1 = np.minimum(c0 + block, N) - 1
+    L = N if seqlen_k is None else int(min(max(seqlen_k, 0), N))
+    hi = np.full_like(r1, L - 1)
+    if causal:
+        hi = np.minimum(hi, r1)
+    lo = np.zeros_like(r0)
+    if window is not None:
+        hi = np.minimum(hi, r1 + int(window[1]))
+        lo = np.maximum(lo, r0 - int(window[0]))
+    t = np.maximum(c0, lo) <= np.minimum(c1, hi)
+    if block_mask is not None:
+        t = t & (np.asarray(block_mask)[:nb, :nb] != 0)
+    return t
+
+
+def visited_tiles(B: int, Hq: int, N: int, *, causal=False, seqlens=None, block_mask=None,
+                  block=128, window=None) -> int:
+    """Number of 128 x 128 tiles with at least one allowed pair."""
     total = 0
     for b in range(B):
-        L = N if seqlens is None else int(min(max(seqlens[b], 0), N))
-        t = kb * block < L
-        if causal:
-            t = t & (kb <= qb)
-        if block_mask is not None:
-            t = t & (np.asarray(block_mask)[:nb, :nb] != 0)
-        total += int(np.broadcast_to(t, (nb, nb)).sum())
+        L = None if seqlens is None else int(seqlens[b])
+        total += int(tile_map(N, causal=causal, seqlen_k=L, block_mask=block_mask, block=block,
+                              window=window).sum())
     return total * Hq
 
 

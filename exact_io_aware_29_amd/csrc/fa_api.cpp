@@ -51,6 +51,9 @@ int check_params(const fa_params* p) {
   const int64_t grid_q = blocks * p->heads_q * p->batch;
   if (grid_q >= (int64_t(1) << 31) || (int64_t)p->batch * p->heads_q * p->seqlen >= (int64_t(1) << 40))
     return fail(FA_ERR_SHAPE, "problem too large to index");
+  if (p->window && (p->window_left < 0 || p->window_right < 0))
+    return fail(FA_ERR_MASK, "window widths must be >= 0 (got %d, %d)", p->window_left,
+                p->window_right);
   if (p->block_mask && p->block_mask_ld < blocks)
     return fail(FA_ERR_MASK, "block_mask_ld %d < ceil(seqlen/128) = %lld", p->block_mask_ld,
                 (long long)blocks);
@@ -82,6 +85,10 @@ fa::Problem make_problem(const fa_params* p) {
   pr.bm_ld = p->block_mask_ld;
   pr.nlb = (int)ceil_div(p->seqlen, 128);
   pr.logw = (int)ceil_div(pr.nlb, 32);
+  // Band widths; without a window (or beyond the sequence) the band covers
+  // every key, and the kernels apply it unconditionally.
+  pr.wl = p->window ? (int)std::min<int64_t>(p->window_left, p->seqlen) : p->seqlen;
+  pr.wr = p->window ? (int)std::min<int64_t>(p->window_right, p->seqlen) : p->seqlen;
   return pr;
 }
 

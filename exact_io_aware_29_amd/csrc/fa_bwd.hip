@@ -154,10 +154,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
   if (k0 < kvalid) {  // else every key of the block is masked: dK = dV = 0
-    // Steps run over (query head of the group) x (query block); rows above
-    // the diagonal see none of these keys under the causal mask.
-    const int qfirst = p.causal ? k0 / C::BQ : 0;
-    const int nq = (p.N + C::BQ - 1) / C::BQ - qfirst;
+    // Steps run over (query head of the group) x (query block), limited to
+    // the rows that can see a key of this block: from the causal diagonal or
+    // the right window edge, up to the left window edge.
+    const int qfirst = max(p.causal ? k0 : 0, k0 - p.wr) / C::BQ;
+    const int qend = min(p.N, k0 + C::BK + p.wl);
+    const int nq = max(0, (qend + C::BQ - 1) / C::BQ - qfirst);
     const int nsteps = p.G * nq;
     auto next_step = [&](int st) {
       while (st < nsteps && !block_on(p.bm, p.bm_ld, (qfirst + st % nq) * C::BQ, k0)) ++st;
@@ -234,7 +236,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       if (nx < nsteps) issue(nx, fill);  // lands during this step
       if (a.log_kv && tid == 0)
         log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
-      const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid);
+      const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid) ||
+                             (q0b + C::BQ - 1 > k0 + p.wl) || (q0b < k0 + C::BK - 1 - p.wr);
 
       // Straight-line step (no per-sub-tile branches): all S and dP products,
       // one uniform mask block, then P / dS and the dV, dK products, so the
@@ -283,7 +286,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int qi = q0b + 32 * (g0 + uu) + perm_row(r, hh);
-              const bool kill = (causal & (my_k > qi)) | kpad;  // branch-free select
+              const bool kill = (causal & (my_k > qi)) | kpad |  // branch-free select
+                                (my_k < qi - p.wl) | (my_k > qi + p.wr);
               s[uu][r] = kill ? 0.f : s[uu][r];
             }
         }
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
   const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
-  const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
+  const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
   const int ntiles = (kend + C::BC - 1) / C::BC;
   const int64_t log_row =
       a.log_q ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
   };
 
-  int kt = next_visit(0);
+  int kt = next_visit(max(0, q0 - p.wl) / C::BC);
   if (kt < ntiles) {
     issue(kt, smem[0]);
     wait_dma();
@@ -433,7 +437,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const int nxt = next_visit(kt + 1);
     if (nxt < ntiles) issue(nxt, fill);
     if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
-    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
+                           (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
 #pragma unroll
     for (int t = 0; t < C::NSUB; ++t) {
       f32x16 st = f32x16{}, dpt = f32x16{};
@@ -459,7 +464,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);
-          const bool kill = (causal & (key > my_q)) | (key >= kvalid);  // branch-free select
+          const bool kill = (causal & (key > my_q)) | (key >= kvalid) |  // branch-free select
+                            (key < my_q - p.wl) | (key > my_q + p.wr);
           st[r] = kill ? 0.f : st[r];
         }
       }

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const T* Vp = static_cast<const T*>(a.v) + b * a.sv.b + hk * a.sv.h;
 
   const int kvalid = valid_keys(p.seqlens, b, p.N);
-  const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
+  const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
   const int ntiles = (kend + C::BC - 1) / C::BC;
 
   // This lane's query row as the B operand of S^T = K Q^T.
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const int64_t log_row =
       a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  for (int kt = max(0, q0 - p.wl) / C::BC; kt < ntiles; ++kt) {
     const int key0 = kt * C::BC;
     if (!block_on(p.bm, p.bm_ld, q0, key0)) continue;  // uniform per workgroup
     __syncthreads();
@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       for (int kk = 0; kk < C::NKK; ++kk) s[t] = mfma(frag<T>(krow + kk * C::KC), qf[kk], s[t]);
     }
 
-    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
+                           (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
     if (__builtin_expect(need_mask, false)) {  // boundary tiles only
       const bool causal = p.causal != 0;
 #pragma unroll
@@ -113,7 +114,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);
-          const bool kill = (causal & (key > my_q)) | (key >= kvalid);  // branch-free select
+          const bool kill = (causal & (key > my_q)) | (key >= kvalid) |  // branch-free select
+                            (key < my_q - p.wl) | (key > my_q + p.wr);
           s[t][r] = kill ? -kInf : s[t][r];
         }
     }
@@ -246,8 +248,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
                              (uint32_t)(p.N - 1) * vsb + 2 * D);
 
   const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
-  const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
+  // Keys any row of the block may see: causal / padding / right window edge
+  // bound the end, the left window edge the start.
+  const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
   const int ntiles = (kend + C::BC - 1) / C::BC;
+  const int kfirst = max(0, q0 - p.wl) / C::BC;
 
   bf16x8 qf[C::NKK];
   {
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
   };
 
-  int kt = next_visit(0);
+  int kt = next_visit(kfirst);
   if (kt < ntiles) {
     issue(kt, smem[0]);
     wait_dma();
@@ -299,7 +304,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     const int nxt = next_visit(kt + 1);
     if (nxt < ntiles) issue(nxt, fill);  // lands while this tile is computed
     if (a.log && tid == 0) log_tile(a.log, log_row, key0);
-    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
+                           (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
 
     // One straight-line block per tile (no per-sub-tile branches), so the
     // compiler can overlap one sub-tile's exponentials with its neighbour's
@@ -337,7 +343,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);
-          const bool kill = (causal & (key > my_q)) | (key >= kvalid);  // branch-free select
+          const bool kill = (causal & (key > my_q)) | (key >= kvalid) |  // branch-free select
+                            (key < my_q - p.wl) | (key > my_q + p.wr);
           s[t][r] = kill ? -kInf : s[t][r];
         }
     }

@@ -21,6 +21,8 @@ struct Problem {
   int bm_ld;
   int nlb;   // ceil(N / 128): 128-blocks per sequence
   int logw;  // uint32 words per tile-log row: ceil(nlb / 32)
+  int wl, wr;  // sliding window: key j allowed for query i iff i - wl <= j <= i + wr
+               // (both in [0, N]; N when there is no window)
 };
 
 struct FwdArgs {

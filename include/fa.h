@@ -106,6 +106,16 @@ typedef struct fa_params {
                                 values are clamped to [0, seqlen] */
   const uint8_t* block_mask; /* device [ceil(N/128)][block_mask_ld], or NULL */
   int32_t block_mask_ld;     /* row pitch of block_mask in bytes */
+  /* Sliding-window (local) attention, ANDed with the masks above: when
+   * `window` is nonzero, key j is allowed for query i only if
+   * i - window_left <= j <= i + window_right (both >= 0; FA_ERR_MASK
+   * otherwise). The synthesis page lists the sliding window among the
+   * attention variants (section 5, item 1) and the tutorial page among the
+   * block-skipping sparse patterns ("sparse attention"). A zero-initialised
+   * struct has no window. */
+  int32_t window;
+  int32_t window_left;
+  int32_t window_right;
 } fa_params;
 
 /*

@@ -63,9 +63,12 @@ def check_grad(g: np.ndarray, ref: np.ndarray, name: str, what=""):
     return r
 
 
-def expected_tiles(B, Hq, N, causal, seqlens, block_mask) -> np.ndarray:
+def expected_tiles(B, Hq, N, causal, seqlens, block_mask, window=None) -> np.ndarray:
     """bool [B, Hq, nlb, nlb]: 128 x 128 tiles holding at least one allowed
-    (query, key) pair, derived from the mask definitions."""
+    (query, key) pair, derived from the mask definitions. With a sliding
+    window (left, right), query row i allows keys i - left .. i + right, so
+    the rows q0..q1 of a row block allow at most keys q0 - left .. q1 + right
+    (and .. q1 under causal), every one of which some row of the block sees."""
     nlb = -(-N // 128)
     qb = np.arange(nlb)[:, None]
     kb = np.arange(nlb)[None, :]
@@ -75,6 +78,10 @@ def expected_tiles(B, Hq, N, causal, seqlens, block_mask) -> np.ndarray:
         t = kb * 128 < L
         if causal:
             t = t & (kb <= qb)
+        if window is not None:
+            first_row, last_row = qb * 128, np.minimum(qb * 128 + 127, N - 1)
+            first_key, last_key = kb * 128, kb * 128 + 127
+            t = t & (last_key >= first_row - window[0]) & (first_key <= last_row + window[1])
         if block_mask is not None:
             t = t & (np.asarray(block_mask)[:nlb, :nlb] != 0)
         out[b] = np.broadcast_to(t, (nlb, nlb))
@@ -102,7 +109,8 @@ def oracle_heads(inp, heads, *, backward=True, q_rows=None, k_rows=None):
     res = {}
     kv_done = set()
     for (b, h) in heads:
-        m = OA.mask_for(b, causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask)
+        m = OA.mask_for(b, causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask,
+                        window=inp.window)
         g = h // G
         q = inp.as_f64("q", (b, h))
         k = inp.as_f64("k", (b, g))

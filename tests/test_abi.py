@@ -97,6 +97,8 @@ def _fwd(p, q=P16, k=P32, v=P48, o=P64, lse=P80, sq=None, sk=None, so=None, log=
     (dict(dtype=7), _abi.FA_ERR_DTYPE),
     (dict(dtype=_abi.FA_FP32, o_dtype=_abi.FA_BF16), _abi.FA_ERR_DTYPE),
     (dict(block_mask=0x9000, block_mask_ld=2), _abi.FA_ERR_MASK),
+    (dict(window=(-1, 4)), _abi.FA_ERR_MASK),
+    (dict(window=(3, -2)), _abi.FA_ERR_MASK),
     (dict(batch=1 << 20, heads_q=1 << 10, heads_kv=1 << 10, seqlen=1 << 20), _abi.FA_ERR_SHAPE),
 ])
 def test_fwd_rejects_bad_params(mut, code):
@@ -153,3 +155,13 @@ def test_size_queries():
     assert fa.fa_bwd_workspace_size(p) == 2 * (2 * 4 * 4097) * 4
     assert fa.fa_tile_log_words(_params(head_dim=80)) == 0
     assert fa.fa_bwd_workspace_size(_params(heads_q=3)) == 0
+
+
+def test_params_struct_window_fields():
+    """A zero-initialised fa_params has no window; make_params fills the flag
+    and both widths."""
+    z = _abi.Params()
+    assert z.window == 0
+    p = _params(window=(12, 0))
+    assert (p.window, p.window_left, p.window_right) == (1, 12, 0)
+    assert _params().window == 0

@@ -40,6 +40,26 @@ def test_pair_counts_match_brute_force(N, causal, L, bm):
     assert list(ours) == ref
 
 
+@pytest.mark.parametrize("N,causal,L,win", [
+    (37, False, None, (3, 2)), (37, True, None, (5, 0)), (40, True, 31, (9, 4)),
+    (29, False, 20, (0, 0)), (33, False, None, (40, 40)),
+])
+def test_window_pair_counts_and_tiles_match_brute_force(N, causal, L, win):
+    block = 8
+    ours = acc.allowed_pairs_per_row(N, causal=causal, seqlen_k=L, block=block, window=win)
+    ref = [sum(brute.allowed(i, j, causal, L, None, block, win) for j in range(N))
+           for i in range(N)]
+    assert list(ours) == ref
+    nb = -(-N // block)
+    tiles = acc.tile_map(N, causal=causal, seqlen_k=L, block=block, window=win)
+    for a in range(nb):
+        for c in range(nb):
+            any_pair = any(brute.allowed(i, j, causal, L, None, block, win)
+                           for i in range(a * block, min(N, a * block + block))
+                           for j in range(c * block, min(N, c * block + block)))
+            assert tiles[a, c] == any_pair, (a, c)
+
+
 def test_workload_flop_counts():
     """Forward = 4 d pairs; backward = 10 d pairs (five products)."""
     w2 = WORKLOADS[2]

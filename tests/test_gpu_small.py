@@ -33,6 +33,16 @@ CASES = [
     (1, 8, 2, 256, 128, False, None, None),
 ]
 
+# Sliding-window (local) attention: (case as above, (left, right) band).
+WINDOW_CASES = [
+    ((2, 2, 2, 300, 64, False, None, None), (37, 5)),
+    ((1, 4, 2, 520, 128, True, None, None), (100, 0)),
+    ((2, 2, 1, 700, 128, True, "random", None), (200, 0)),
+    ((1, 2, 2, 640, 64, False, None, "random"), (130, 60)),
+    ((1, 2, 2, 257, 64, True, None, None), (0, 0)),
+    ((2, 4, 4, 384, 128, False, [384, 130], None), (0, 3)),
+]
+
 
 def _ids(c):
     B, Hq, Hkv, N, d, causal, sl, bm = c
@@ -45,13 +55,14 @@ def _run(inp, o_dtype=None, tile_log=True):
     sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).cuda()
     bm = None if inp.block_mask is None else torch.from_numpy(inp.block_mask).cuda()
     o, lse, log = fa.fa_fwd(q, k, v, scale=inp.scale, causal=w.causal, seqlens_k=sl,
-                            block_mask=bm, o_dtype=o_dtype, tile_log=tile_log)
+                            block_mask=bm, o_dtype=o_dtype, tile_log=tile_log, window=inp.window)
     return (q, k, v, sl, bm), o, lse, log
 
 
 def _oracle_full(inp, backward=True):
     w = inp.workload
-    kw = dict(causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask)
+    kw = dict(causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask,
+              window=inp.window)
     q, k, v = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
     o, lse = oracle.attention_forward(q, k, v, inp.scale, **kw)
     if not backward:
@@ -62,16 +73,26 @@ def _oracle_full(inp, backward=True):
 
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 def test_small_fwd_bwd_bf16(case):
+    _check_bf16(case, None)
+
+
+@pytest.mark.parametrize("case,window", WINDOW_CASES,
+                         ids=[f"{_ids(c)}w{w[0]}-{w[1]}" for c, w in WINDOW_CASES])
+def test_small_sliding_window_bf16(case, window):
+    _check_bf16(case, window)
+
+
+def _check_bf16(case, window):
     B, Hq, Hkv, N, d, causal, sl, bm = case
     inp = draw_case(B, Hq, Hkv, N, d, "bf16", causal=causal, seqlens=sl, block_mask=bm,
-                    seed=N + d + Hq)
-    print(f"case {_ids(case)}", flush=True)
+                    seed=N + d + Hq, window=window)
+    print(f"case {_ids(case)} window {window}", flush=True)
     o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = _oracle_full(inp)
     (q, k, v, slt, bmt), o, lse, log = _run(inp)
     torch.cuda.synchronize()
     check_o(host64(o), o_ref, True, "bf16-O")
     check_lse(host64(lse), lse_ref, TOL_BF16_LSE)
-    exp_tiles = expected_tiles(B, Hq, N, causal, inp.seqlens, inp.block_mask)
+    exp_tiles = expected_tiles(B, Hq, N, causal, inp.seqlens, inp.block_mask, window)
     assert np.array_equal(decode_log(log, B, Hq, N), exp_tiles), "forward tile set"
 
     o32, lse32, _ = _run(inp, o_dtype=torch.float32, tile_log=False)[1:]
@@ -80,7 +101,7 @@ def test_small_fwd_bwd_bf16(case):
 
     do = dev(inp.do, "bf16")
     dq, dk, dv, blog = fa.fa_bwd(q, k, v, o, lse, do, scale=inp.scale, causal=causal,
-                                 seqlens_k=slt, block_mask=bmt, tile_log=True)
+                                 seqlens_k=slt, block_mask=bmt, tile_log=True, window=window)
     torch.cuda.synchronize()
     check_grad(host64(dq), dq_ref, "dQ")
     check_grad(host64(dk), dk_ref, "dK")
@@ -91,7 +112,7 @@ def test_small_fwd_bwd_bf16(case):
 
     # the backward also accepts an fp32 O
     dq2, dk2, dv2, _ = fa.fa_bwd(q, k, v, o32, lse32, do, scale=inp.scale, causal=causal,
-                                 seqlens_k=slt, block_mask=bmt)
+                                 seqlens_k=slt, block_mask=bmt, window=window)
     torch.cuda.synchronize()
     check_grad(host64(dq2), dq_ref, "dQ(fp32 O)")
     check_grad(host64(dk2), dk_ref, "dK(fp32 O)")
@@ -109,10 +130,21 @@ FP32_CASES = [
 
 @pytest.mark.parametrize("case", FP32_CASES, ids=_ids)
 def test_small_fwd_fp32(case):
+    _check_fp32(case, None)
+
+
+@pytest.mark.parametrize("case,window", [((1, 2, 1, 300, 128, True, None, None), (50, 0)),
+                                         ((1, 1, 1, 200, 64, False, "random", None), (7, 90))],
+                         ids=["causal-w50", "w7-90pad"])
+def test_small_sliding_window_fp32(case, window):
+    _check_fp32(case, window)
+
+
+def _check_fp32(case, window):
     B, Hq, Hkv, N, d, causal, sl, bm = case
     inp = draw_case(B, Hq, Hkv, N, d, "fp32", causal=causal, seqlens=sl, block_mask=bm,
-                    seed=3 * N + d, with_do=False)
-    print(f"case {_ids(case)}", flush=True)
+                    seed=3 * N + d, with_do=False, window=window)
+    print(f"case {_ids(case)} window {window}", flush=True)
     o_ref, lse_ref, _ = _oracle_full(inp, backward=False)
     _, o, lse, log = _run(inp)
     torch.cuda.synchronize()
@@ -120,7 +152,7 @@ def test_small_fwd_fp32(case):
     assert err <= TOL_FP32_O, f"fp32 O max abs err {err:.3g}"
     check_lse(host64(lse), lse_ref, TOL_FP32_LSE)
     assert np.array_equal(decode_log(log, B, Hq, N),
-                          expected_tiles(B, Hq, N, causal, inp.seqlens, inp.block_mask))
+                          expected_tiles(B, Hq, N, causal, inp.seqlens, inp.block_mask, window))
 
 
 def test_strided_bshd_layout():

@@ -26,7 +26,7 @@ def _run(wid):
     q, k, v = dev(inp.q, w.dtype), dev(inp.k, w.dtype), dev(inp.v, w.dtype)
     sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).cuda()
     bm = None if inp.block_mask is None else torch.from_numpy(inp.block_mask).cuda()
-    kw = dict(scale=inp.scale, causal=w.causal, seqlens_k=sl, block_mask=bm)
+    kw = dict(scale=inp.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, window=w.window)
     o, lse, flog = fa.fa_fwd(q, k, v, tile_log=True, **kw)
     res = dict(inp=inp, o=o, lse=lse, flog=flog)
     if w.backward:
@@ -40,7 +40,8 @@ def _run(wid):
 def _check_tiles(res):
     inp = res["inp"]
     w = inp.workload
-    exp = expected_tiles(w.batch, w.heads_q, w.seqlen, w.causal, inp.seqlens, inp.block_mask)
+    exp = expected_tiles(w.batch, w.heads_q, w.seqlen, w.causal, inp.seqlens, inp.block_mask,
+                         w.window)
     assert np.array_equal(decode_log(res["flog"], w.batch, w.heads_q, w.seqlen), exp), "fwd tiles"
     if w.backward:
         half = res["blog"].numel() // 2
@@ -140,3 +141,17 @@ def test_workload5_butterfly_block_sparse():
                              np.arange(65536 - 128, 65536, 5)])
     k_rows = np.arange(3 * 128, 4 * 128)
     _compare(res, [(0, 0), (0, 7)], q_rows=q_rows, k_rows=k_rows)
+
+
+def test_workload6_sliding_window():
+    """Causal local attention, 1023 keys back, N = 8192, d = 128."""
+    res = _run(6)
+    frac = _check_tiles(res)
+    assert 0.1 < frac < 0.2  # 9 or 10 visited 128-blocks of 64 per row block
+    _check_invariants(res)
+    rng = np.random.default_rng(66)
+    N = 8192
+    q_rows = np.unique(np.concatenate([[0, 1, 1022, 1023, 1024, 1025, 4095, 4096, 8191],
+                                       rng.integers(0, N, 40)]))
+    k_rows = np.concatenate([np.arange(0, 8), np.arange(4090, 4100), np.arange(N - 8, N)])
+    _compare(res, [(0, 0), (3, 15)], q_rows=q_rows, k_rows=k_rows)
