@@ -7,6 +7,7 @@ with it.
 from .attention import (  # noqa: F401
     MaskSpec,
     attention_backward,
+    attention_decode,
     attention_forward,
     head_backward,
     head_forward,

@@ -216,6 +216,28 @@ def attention_forward(q, k, v, scale, *, causal=False, seqlens=None,
     return o, lse
 
 
+def attention_decode(q, k, v, scale, *, seqlens=None):
+    """Decoding: one query row per head against a key/value cache.
+
+    q: [B, Hq, d], k/v: [B, Hkv, N, d]. The query sees cached keys
+    0 .. L_b - 1 (L_b = seqlens[b], or N). Returns O [B, Hq, d] and
+    LSE [B, Hq]. This is the forward above for a single row (the synthesis
+    page, section 3 item 4: in decoding the score matrix is one row per
+    head); the split-and-merge of the GPU path is not reproduced here.
+    """
+    B, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    o = np.zeros((B, Hq, v.shape[3]))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        m = mask_for(b, seqlens=seqlens)
+        for h in range(Hq):
+            ob, lb = head_forward(q[b, h][None, :], k[b, h // G], v[b, h // G], scale, m,
+                                  rows=[0])
+            o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse
+
+
 def attention_backward(q, k, v, do, scale, *, causal=False, seqlens=None,
                        block_mask=None, mask_block=128, window=None):
     """Whole-tensor backward. Returns dQ [B,Hq,N,d], dK, dV [B,Hkv,N,d]."""

@@ -48,6 +48,7 @@ class Workload:
     butterfly: bool = False
     backward: bool = True
     window: Optional[tuple] = None  # (left, right) sliding-window band
+    decode: bool = False  # one query row per head against `seqlen` cached keys
 
     @property
     def group(self) -> int:
@@ -74,6 +75,9 @@ class Workload:
             parts.append("butterfly128")
         if self.window is not None:
             parts.append(f"window{self.window[0]}-{self.window[1]}")
+        if self.decode:
+            parts.append("decode")
+            return " ".join(parts)
         parts.append("fwd+bwd" if self.backward else "fwd")
         return " ".join(parts)
 
@@ -90,6 +94,11 @@ WORKLOADS = {
     # it (a sliding window; no such shape is fixed by the pages).
     6: Workload("sliding-window-8k", 4, 16, 16, 8192, 128, "bf16", causal=True,
                 window=(1023, 0)),
+    # Decoding: one new query row per head against a GQA key/value cache of
+    # up to 32K positions per sequence (cache lengths uniform over
+    # [16384, 32768]); the pages fix no such shape.
+    7: Workload("decode-32k-gqa", 16, 32, 8, 32768, 128, "bf16", pad_range=(16384, 32768),
+                backward=False, decode=True),
 }
 
 
@@ -152,7 +161,7 @@ def draw(w: Workload, seed: int, *, with_do: Optional[bool] = None) -> Inputs:
     """Draw the inputs of workload ``w`` from ``numpy.random.default_rng(seed)``."""
     rng = np.random.default_rng(seed)
     with_do = w.backward if with_do is None else with_do
-    qshape = (w.batch, w.heads_q, w.seqlen, w.head_dim)
+    qshape = (w.batch, w.heads_q, 1 if w.decode else w.seqlen, w.head_dim)
     kshape = (w.batch, w.heads_kv, w.seqlen, w.head_dim)
 
     def one(shape):

@@ -363,6 +363,46 @@ def test_bf16_inputs_widen_exactly():
     assert np.all(mant * 2 ** 8 == np.round(mant * 2 ** 8))
 
 
+# ---------------------------------------------------------------- decode pins
+
+def test_decode_brute_force_and_closed_forms():
+    """Decoding (one query row against a cache): the scalar brute force for
+    several cache lengths; Q = 0 gives the mean of the first L values and
+    LSE = ln L; an empty cache gives O = 0, LSE = -inf."""
+    rng = np.random.default_rng(71)
+    B, Hq, Hkv, n, d = 3, 4, 2, 11, 5
+    q, k, v = rand(B, Hq, d, rng=rng), rand(B, Hkv, n, d, rng=rng), rand(B, Hkv, n, d, rng=rng)
+    L = np.array([11, 4, 0])
+    o, lse = oracle.attention_decode(q, k, v, 0.45, seqlens=L)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // 2
+            bo, bl = brute.forward([q[b, h].tolist()], k[b, g].tolist(), v[b, g].tolist(), 0.45,
+                                   seqlen_k=int(L[b]))
+            np.testing.assert_allclose(o[b, h], bo[0], atol=1e-13)
+            if L[b] == 0:
+                assert np.isneginf(lse[b, h]) and not o[b, h].any()
+            else:
+                np.testing.assert_allclose(lse[b, h], bl[0], atol=1e-13)
+    o0, l0 = oracle.attention_decode(np.zeros_like(q), k, v, 0.45, seqlens=L)
+    for b in range(2):
+        np.testing.assert_allclose(o0[b], np.repeat(v[b, :, :L[b]].mean(axis=1), 2, axis=0),
+                                   atol=1e-14)
+        np.testing.assert_allclose(l0[b], math.log(L[b]), atol=1e-14)
+
+
+def test_decode_is_the_last_row_of_causal_attention():
+    """With the whole cache visible, decoding the last position's query
+    equals the last row of causal attention over the sequence."""
+    rng = np.random.default_rng(72)
+    B, Hq, Hkv, n, d = 2, 4, 1, 9, 6
+    q, k, v = rand(B, Hq, n, d, rng=rng), rand(B, Hkv, n, d, rng=rng), rand(B, Hkv, n, d, rng=rng)
+    of, lf = oracle.attention_forward(q, k, v, 0.3, causal=True)
+    od, ld = oracle.attention_decode(q[:, :, -1], k, v, 0.3)
+    np.testing.assert_allclose(od, of[:, :, -1], atol=1e-14)
+    np.testing.assert_allclose(ld, lf[:, :, -1], atol=1e-14)
+
+
 # ---------------------------------------------------------------- mutants
 
 def _pins_pass():
