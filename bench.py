@@ -25,7 +25,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd & fwd+bwd TFLOP/s + % of bf16 MFMA peak, B64 H16 N1024 d64"
+DECODE_METRIC = ("decode attention KV-cache read GB/s (one query row per head), "
+                 "B16 Hq32 Hkv8 cache 32K d128")
 KERNEL_SOURCES = {
+    "decode": ["fa_decode.hip", "fa_stage.h", "fa_device.h"],
     "fwd": ["fa_fwd.hip", "fa_stage.h", "fa_device.h"],
     "bwd_dkdv": ["fa_bwd.hip", "fa_stage.h", "fa_device.h"],
     "bwd_dq": ["fa_bwd.hip", "fa_stage.h", "fa_device.h"],
@@ -39,7 +42,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2,
-                    help="workload id (2 = the headline B64 H16 N1024 d64 shape)")
+                    help="workload id (2 = the headline B64 H16 N1024 d64 shape; 7 = decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -114,6 +117,108 @@ def cpu_baseline(inp, pairs_per_head, budget_s):
     }
 
 
+def decode_cpu_baseline(inp, budget_s):
+    """Time the fp64 oracle's decode batch entry by batch entry until the
+    budget is spent; report GB/s of the same algorithmic bytes."""
+    import oracle
+    from exact_io_aware_29_amd import accounting as acc
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    w = inp.workload
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        sl = slice(b, b + 1)
+        oracle.attention_decode(inp.as_f64("q", (sl,))[:, :, 0, :], inp.as_f64("k", (sl,)),
+                                inp.as_f64("v", (sl,)), inp.scale, seqlens=inp.seqlens[sl])
+        done += 1
+        nbytes += acc.decode_bytes(1, w.heads_q, w.heads_kv, w.head_dim, inp.seqlens[sl])
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fp64 oracle decode of the first {done} of {w.batch} sequences, "
+                      f"{el:.1f} s; same algorithmic bytes"}
+
+
+def decode_main(args, w, inp, dev):
+    """One step = one fa_decode call (split kernel + combine) over the batch."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_29_amd as fa
+    from exact_io_aware_29_amd import accounting as acc
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = t(inp.q), t(inp.k), t(inp.v)
+    sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    p = fa.make_params(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv, seqlen=w.seqlen,
+                       head_dim=w.head_dim)
+    ws = torch.empty(fa.fa_decode_workspace_size(p) // 4 + 4, dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_decode(q, k, v, scale=inp.scale, seqlens_k=sl, out=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events[i][0].record()
+        step()
+        events[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([events[i][0].elapsed_time(events[i][1]) for i in range(args.steps)]))
+    lens = inp.seqlens if inp.seqlens is not None else [w.seqlen] * w.batch
+    nbytes = acc.decode_bytes(w.batch, w.heads_q, w.heads_kv, w.head_dim, lens)
+    ms_step = wall / args.steps * 1e3
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    ach = nbytes / (ms * 1e-3) / 1e9
+    kernels = {"decode": {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1),
+                          "peak": acc.HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(ach / acc.HBM_PEAK_GBS, 4)}}
+    rec = {
+        "metric": DECODE_METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, rounded to bf16)",
+        "config": {"workload": w.describe(), "batch": w.batch, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "cache_len": w.seqlen, "head_dim": w.head_dim,
+                   "pass": "decode"},
+        "algorithmic_bytes": nbytes,
+        "kernels": kernels,
+        "roofline": dict(kernel="decode", **{k_: kernels["decode"][k_] for k_ in
+                                             ("bound", "achieved", "peak", "unit", "frac")},
+                         traffic=recorded_traffic("decode", args.workload)),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = decode_cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -132,6 +237,9 @@ def main():
     w = WORKLOADS[args.workload]
     inp = draw(w, args.workload)
     dev = torch.device("cuda:0")
+    if w.decode:
+        decode_main(args, w, inp, dev)
+        return
 
     def t(a):
         if w.dtype == "bf16":

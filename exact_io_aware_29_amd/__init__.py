@@ -21,7 +21,8 @@ import torch
 from . import _abi
 from ._abi import FA_BF16, FA_FP32, FA_MASK_BLOCK, Params, Strides  # noqa: F401
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_tile_log_words", "fa_strerror",
+__all__ = ["fa_fwd", "fa_bwd", "fa_decode", "fa_bwd_workspace_size", "fa_decode_workspace_size",
+           "fa_tile_log_words", "fa_strerror",
            "FAError", "make_params", "library"]
 
 
@@ -177,3 +178,47 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
     if st != 0:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv, log
+
+
+def fa_decode_workspace_size(params: Params) -> int:
+    return _abi.load().fa_decode_workspace_size(ctypes.byref(params))
+
+
+def fa_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+              seqlens_k: Optional[torch.Tensor] = None, o_dtype: Optional[torch.dtype] = None,
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None):
+    """Decode attention: q [B, Hq, 1, d] (one new row per head) against the
+    cache k, v [B, Hkv, N, d]. Returns (O [B, Hq, 1, d], LSE [B, Hq])."""
+    lib = _abi.load()
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q must be [batch, heads_q, 1, head_dim]")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("decode takes bf16 q, k, v")
+    B, Hq, _, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k/v must be [batch, heads_kv, seqlen, head_dim] matching q")
+    sl_ptr = 0
+    if seqlens_k is not None:
+        if seqlens_k.dtype != torch.int32 or seqlens_k.numel() < B or not seqlens_k.is_contiguous():
+            raise ValueError("seqlens_k must be a contiguous int32 tensor of length >= batch")
+        sl_ptr = seqlens_k.data_ptr()
+    odt = FA_BF16 if o_dtype is None else _DT[o_dtype]
+    p = make_params(dtype=FA_BF16, o_dtype=odt, batch=B, heads_q=Hq, heads_kv=k.shape[1],
+                    seqlen=k.shape[2], head_dim=d, scale=scale, seqlens_k=sl_ptr)
+    if out is None:
+        out = torch.empty((B, Hq, 1, d), dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.numel() != B * Hq:
+        raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
+    need = lib.fa_decode_workspace_size(ctypes.byref(p))
+    if need and workspace is None:
+        workspace = torch.empty(need // 4 + 4, dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.fa_decode(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                       _strides(v), _ptr(out), _strides(out), _ptr(lse), _ptr(workspace),
+                       ws_bytes, _stream())
+    if st != 0:
+        raise FAError(st, "fa_decode")
+    return out, lse

@@ -60,6 +60,9 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
     "fa_bwd": (ctypes.c_int, [ctypes.POINTER(Params), _P, _S, _P, _S, _P, _S, _P, _S, _P, _S, _P,
                               _P, _S, _P, _S, _P, _S, _P, ctypes.c_size_t, _P, _P, _P]),
+    "fa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
+    "fa_decode": (ctypes.c_int, [ctypes.POINTER(Params), _P, _S, _P, _S, _P, _S, _P, _S, _P, _P,
+                                 ctypes.c_size_t, _P]),
     "fa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }

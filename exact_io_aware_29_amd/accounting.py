@@ -112,6 +112,15 @@ def visited_tiles(B: int, Hq: int, N: int, *, causal=False, seqlens=None, block_
     return total * Hq
 
 
+def decode_bytes(B: int, Hq: int, Hkv: int, d: int, cache_lens, eb: int = 2,
+                 o_eb: int = 2) -> int:
+    """Compulsory HBM bytes of one decode step: each sequence's cached K and
+    V rows 0 .. L_b - 1 read once, the query rows read, the output rows and
+    the float32 LSE written."""
+    kv = sum(int(L) for L in cache_lens) * Hkv * d * eb * 2
+    return kv + B * Hq * d * eb + B * Hq * d * o_eb + B * Hq * 4
+
+
 def flops(pairs: int, d: int) -> dict:
     """Algorithmic flops of the forward, backward and per-kernel shares."""
     return {

@@ -5,6 +5,7 @@
 // machine without one).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -220,6 +221,88 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = fa::launch_bwd_dq(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_dq launch");
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event record");
+  return FA_OK;
+}
+
+namespace {
+
+// Decode work split: enough (batch, key/value head, block of 16 query heads,
+// key split) units for several workgroups per CU, every split at least four
+// 64-key tiles and a multiple of 64 keys.
+struct DecodePlan {
+  int hblocks, splits, split_len;
+};
+
+DecodePlan decode_plan(const fa_params* p) {
+  DecodePlan d;
+  const int64_t G = p->heads_q / p->heads_kv;
+  d.hblocks = (int)ceil_div(G, 16);
+  const int64_t units = (int64_t)p->batch * p->heads_kv * d.hblocks;
+  const int64_t max_splits = ceil_div(p->seqlen, 256);
+  const int64_t want = std::max<int64_t>(1, ceil_div(2048, units));
+  const int64_t splits = std::min<int64_t>(max_splits, want);
+  const int64_t len = ceil_div(ceil_div(p->seqlen, splits), 64) * 64;
+  d.split_len = (int)len;
+  d.splits = (int)ceil_div(p->seqlen, len);
+  return d;
+}
+
+int check_decode_params(const fa_params* p) {
+  const int st = check_params(p);
+  if (st != FA_OK) return st;
+  if (p->dtype != FA_BF16) return fail(FA_ERR_DTYPE, "decode supports bf16 inputs only");
+  if (p->block_mask) return fail(FA_ERR_MASK, "decode takes no block mask");
+  if (p->window) return fail(FA_ERR_MASK, "decode takes no sliding window");
+  return FA_OK;
+}
+
+}  // namespace
+
+size_t fa_decode_workspace_size(const fa_params* p) {
+  if (check_decode_params(p) != FA_OK) return 0;
+  const DecodePlan d = decode_plan(p);
+  if (d.splits == 1) return 0;
+  return (size_t)p->batch * p->heads_q * d.splits * (p->head_dim + 1) * sizeof(float);
+}
+
+int fa_decode(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+              const void* v, fa_strides sv, void* o, fa_strides so, float* lse, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  g_detail[0] = '\0';
+  FA_CHECK(check_decode_params(p));
+  FA_CHECK(check_tensor("q", q, sq, p->dtype));
+  FA_CHECK(check_tensor("k", k, sk, p->dtype));
+  FA_CHECK(check_tensor("v", v, sv, p->dtype));
+  FA_CHECK(check_tensor("o", o, so, p->o_dtype));
+  if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
+  const size_t need = fa_decode_workspace_size(p);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need && reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(FA_ERR_ALIGN, "workspace is not 16-byte aligned");
+
+  const DecodePlan d = decode_plan(p);
+  fa::DecodeArgs a;
+  a.p = make_problem(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.sq = conv(sq);
+  a.sk = conv(sk);
+  a.sv = conv(sv);
+  a.so = conv(so);
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = need ? a.ws_o + (size_t)p->batch * p->heads_q * d.splits * p->head_dim : nullptr;
+  a.splits = d.splits;
+  a.split_len = d.split_len;
+  a.hblocks = d.hblocks;
+  a.o_fp32 = p->o_dtype == FA_FP32;
+  const hipError_t e = fa::launch_decode(a, p->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
   return FA_OK;
 }
 

@@ -56,10 +56,27 @@ struct BwdArgs {
   int o_fp32;
 };
 
+// Decode: one query row per head (q, o: [B][Hq][.][d], row index 0 only)
+// against a cache of N keys, split into `splits` ranges of `split_len` keys.
+struct DecodeArgs {
+  Problem p;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  Strides sq, sk, sv, so;
+  float* lse;     // [B][Hq], natural log
+  float* ws_o;    // workspace: per-split normalised partials [B][Hq][splits][d]
+  float* ws_lse;  // workspace: per-split log2-sum-exp [B][Hq][splits]
+  int splits, split_len, hblocks;
+  int o_fp32;
+};
+
 // Launchers (defined next to their kernels). dtype: 0 bf16, 1 fp32.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s);
 
 }  // namespace fa

@@ -192,6 +192,35 @@ int fa_bwd(const fa_params* p,
            void* const* stage_events,
            void* stream);
 
+/* Bytes of device workspace fa_decode needs for `p` (0 when the keys are
+ * not split; 0 also for invalid parameters). */
+size_t fa_decode_workspace_size(const fa_params* p);
+
+/*
+ * fa_decode -- attention of one new query row per head against a cache of
+ * p->seqlen keys (decoding). The synthesis page (section 3, item 4) notes
+ * that here the score matrix is a single row and the cost is reading the
+ * K/V cache from HBM; the keys are split across workgroups and the partial
+ * results merged with the tutorial page's softmax merge rule (exercise 2).
+ *
+ *   q, o      device [batch][heads_q][.][head_dim] (row index 0 is used;
+ *             the row stride is ignored), q bf16, o of p->o_dtype
+ *   k, v      device [batch][heads_kv][seqlen][head_dim] bf16, the cache
+ *   lse       device float32 [batch][heads_q], natural-log log-sum-exp
+ *             (-inf for an empty cache)
+ *   workspace device buffer of >= fa_decode_workspace_size(p) bytes (may be
+ *             NULL when that is 0), 16-byte aligned, contents ignored
+ *   stream    hipStream_t to enqueue on (NULL = default stream)
+ *
+ * The query sees keys 0 .. L_b - 1, L_b = seqlens_k[b] (clamped to
+ * [0, seqlen]) or seqlen; `causal` has no effect (the new row is the last
+ * position). Requirements and errors as fa_fwd, plus: bf16 inputs only
+ * (FA_ERR_DTYPE); no block mask and no window (FA_ERR_MASK).
+ */
+int fa_decode(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+              const void* v, fa_strides sv, void* o, fa_strides so, float* lse, void* workspace,
+              size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -85,3 +85,10 @@ def test_byte_models_order():
     assert m["bwd_compulsory"] < m["bwd_tile_model"] < m["bwd_alg0"]
     # compulsory forward = Q, K, V read + O written (bf16) + LSE (fp32)
     assert m["fwd_compulsory"] == 4 * 64 * 16 * 1024 * 64 * 2 + 64 * 16 * 1024 * 4
+
+
+def test_decode_bytes():
+    """K and V rows of each cache read once (bf16), q read and o written
+    (bf16), LSE written (fp32)."""
+    n = acc.decode_bytes(2, 8, 2, 128, [100, 0])
+    assert n == 100 * 2 * 128 * 2 * 2 + 2 * 8 * 128 * 2 * 2 + 2 * 8 * 4
