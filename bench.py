@@ -29,6 +29,7 @@ DECODE_METRIC = ("decode attention KV-cache read GB/s (one query row per head), 
                  "B16 Hq32 Hkv8 cache 32K d128")
 KERNEL_SOURCES = {
     "decode": ["fa_decode.hip", "fa_stage.h", "fa_device.h"],
+    "decode_combine": ["fa_decode.hip"],
     "fwd": ["fa_fwd.hip", "fa_stage.h", "fa_device.h"],
     "bwd_dkdv": ["fa_bwd.hip", "fa_stage.h", "fa_device.h"],
     "bwd_dq": ["fa_bwd.hip", "fa_stage.h", "fa_device.h"],
@@ -184,6 +185,7 @@ def decode_main(args, w, inp, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = float(np.mean([events[i][0].elapsed_time(events[i][1]) for i in range(args.steps)]))
+    copy_calibration(args, dev)
     lens = inp.seqlens if inp.seqlens is not None else [w.seqlen] * w.batch
     nbytes = acc.decode_bytes(w.batch, w.heads_q, w.heads_kv, w.head_dim, lens)
     ms_step = wall / args.steps * 1e3
@@ -212,11 +214,33 @@ def decode_main(args, w, inp, dev):
         "kernels": kernels,
         "roofline": dict(kernel="decode", **{k_: kernels["decode"][k_] for k_ in
                                              ("bound", "achieved", "peak", "unit", "frac")},
-                         traffic=recorded_traffic("decode", args.workload)),
+                         traffic=decode_traffic(args.workload)),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = decode_cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def decode_traffic(workload: int):
+    """Counter bytes of one decode pass: the split kernel plus the combine
+    kernel, both inside the timed region (None if either record is stale)."""
+    a = recorded_traffic("decode", workload)
+    b = recorded_traffic("decode_combine", workload)
+    return None if a is None or b is None else a + b
+
+
+def copy_calibration(args, dev):
+    """A plain device copy of known size, run (outside every timed region)
+    so that one counter pass also reads FETCH_SIZE / WRITE_SIZE for it."""
+    if not args.copy_calib_mib:
+        return
+    import torch
+    n = args.copy_calib_mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -286,13 +310,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    if args.copy_calib_mib:
-        n = args.copy_calib_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    copy_calibration(args, dev)
 
     def avg_ms(a, b):
         return float(np.mean([events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)]))

@@ -186,12 +186,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
                                  (uint32_t)(p.N - 1) * qsb + 2 * D);
       const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
                                  (uint32_t)(p.N - 1) * dsb + 2 * D);
+      // Registers are at their limit with the V block in LDS: rebuild the
+      // DMA offsets for this step from a lane index read afresh (an opaque
+      // mbcnt, so neither it nor the offsets are hoisted out of the loop and
+      // kept live, and nothing is reloaded from scratch, which would wait on
+      // the DMA just issued).
+      const int ln = C::VLDS ? fresh_lane_id() : lane;
       if constexpr (C::VLDS) {
-        // Registers are at their limit here: rebuild the DMA offsets for
-        // this step from the lane index (laundered so that they are not
-        // hoisted out of the loop and kept live).
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
         dma_offsets<D, C::BQ>(qvo, qsb, w, ln);
         dma_offsets<D, C::BQ>(dvo, dsb, w, ln);
       }
@@ -203,17 +204,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         const int c = is_d ? w - C::NRC : w;
         const Rsrc rs = make_rsrc((is_d ? a.dvec : a.lse2) + row0, (uint32_t)p.N * 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (FA_LDS void*)(stage + (is_d ? C::DVEC_OFF : C::LSE_OFF) + 256 * c), 4, 4 * lane,
+            rs, (FA_LDS void*)(stage + (is_d ? C::DVEC_OFF : C::LSE_OFF) + 256 * c), 4, 4 * ln,
             (uint32_t)(q0b + 64 * c) * 4, 0, 0);
       }
     };
 
-    // B-operand offsets of this lane's key row in the V block.
-    int vboff[C::VLDS ? C::NKK : 1];
+    const int vb0 = C::VT::off(32 * w + lr, hh);
     if constexpr (C::VLDS) {
       using VT = typename C::VT;
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) vboff[kk] = VT::off(32 * w + lr, 2 * kk + hh);
+      static_assert((VT::RB & (VT::RB - 1)) == 0 && VT::CPR * 16 == VT::RB,
+                    "chunk field below a power-of-two row pitch");
       int vvo[VT::NLD];
       const int vsb = 2 * (int)a.sv.n;
       dma_offsets<D, C::BK>(vvo, vsb, w, lane);
@@ -232,6 +232,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       const char* dOs = Qs + T::BYTES;
       const int h = hk * p.G + sidx / nq;
       const int q0b = (qfirst + sidx % nq) * C::BQ;
+      // B-operand offsets of this lane's key row in the V block. The chunk
+      // field of a swizzled offset lies below the row pitch, so head-dim
+      // step kk (chunk 2 kk + hh) is step 0's offset XOR 32 kk; rebuilt each
+      // step from one live register (all eight kept live across the loop
+      // would push a row offset out to scratch).
+      int vboff[C::VLDS ? C::NKK : 1];
+      if constexpr (C::VLDS) {
+        int v0 = vb0;
+        asm volatile("" : "+v"(v0));
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) vboff[kk] = v0 ^ (32 * kk);
+      }
       const int nx = next_step(sidx + 1);
       if (nx < nsteps) issue(nx, fill);  // lands during this step
       if (a.log_kv && tid == 0)
@@ -280,15 +292,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
             s[uu][r] = __builtin_amdgcn_exp2f(fmaf(s[uu][r], sl2, -lv[r >> 2][r & 3]));
         }
         if (__builtin_expect(need_mask, false)) {  // boundary tiles only
-          const bool kpad = my_k >= kvalid;
+          // Row qi sees key my_k iff qi - wl <= my_k <= qi + hi (hi = 0 under
+          // the causal mask, else the right window edge), i.e. iff
+          // qi - my_k + hi lies in [0, wl + hi]: one unsigned compare per
+          // element against a per-lane base (exact in 32-bit wrap-around for
+          // N <= 2^30).
+          // (The lane terms come from a fresh lane index: this rarely taken
+          // block would otherwise hold them live, or reload them from
+          // scratch, across the whole loop.)
+          const int ln = fresh_lane_id();
+          const int kl = k0 + 32 * w + (ln & 31);  // = my_k
+          const bool kpad = kl >= kvalid;
+          const unsigned hi = causal ? 0u : (unsigned)p.wr;
+          const unsigned span = (unsigned)p.wl + hi;
+          const unsigned base = (unsigned)(q0b + 8 * (ln >> 5)) + hi - (unsigned)kl;
 #pragma unroll
           for (int uu = 0; uu < C::NG; ++uu)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int qi = q0b + 32 * (g0 + uu) + perm_row(r, hh);
-              const bool kill = (causal & (my_k > qi)) | kpad |  // branch-free select
-                                (my_k < qi - p.wl) | (my_k > qi + p.wr);
-              s[uu][r] = kill ? 0.f : s[uu][r];
+              const unsigned t = base + (unsigned)(32 * (g0 + uu) + perm_row(r, 0));
+              s[uu][r] = (kpad | (t > span)) ? 0.f : s[uu][r];  // branch-free select
             }
         }
 #pragma unroll
@@ -461,12 +484,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
       if (__builtin_expect(need_mask, false)) {  // boundary tiles only
+        // Key j is seen iff my_q - wl <= j <= my_q + hi (hi = 0 under the
+        // causal mask, else the right window edge) and j < kvalid; the band
+        // test is one unsigned compare of j - my_q + wl against wl + hi.
+        const unsigned hi = causal ? 0u : (unsigned)p.wr;
+        const unsigned span = (unsigned)p.wl + hi;
+        const unsigned base = (unsigned)(key0 + 32 * t + 8 * hh + p.wl) - (unsigned)my_q;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);
-          const bool kill = (causal & (key > my_q)) | (key >= kvalid) |  // branch-free select
-                            (key < my_q - p.wl) | (key > my_q + p.wr);
-          st[r] = kill ? 0.f : st[r];
+          const bool kill = (base + (unsigned)perm_row(r, 0) > span) | (key >= kvalid);
+          st[r] = kill ? 0.f : st[r];  // branch-free select
         }
       }
 #pragma unroll

@@ -108,15 +108,20 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
                            (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
     if (__builtin_expect(need_mask, false)) {  // boundary tiles only
-      const bool causal = p.causal != 0;
+      // Key j is seen iff my_q - wl <= j <= my_q + hi (hi = 0 under the
+      // causal mask, else the right window edge) and j < kvalid; the band
+      // test is one unsigned compare of j - my_q + wl against wl + hi.
+      const unsigned hi = p.causal ? 0u : (unsigned)p.wr;
+      const unsigned span = (unsigned)p.wl + hi;
+      const unsigned base = (unsigned)(key0 + 8 * hh + p.wl) - (unsigned)my_q;
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);
-          const bool kill = (causal & (key > my_q)) | (key >= kvalid) |  // branch-free select
-                            (key < my_q - p.wl) | (key > my_q + p.wr);
-          s[t][r] = kill ? -kInf : s[t][r];
+          const bool kill =
+              (base + (unsigned)(32 * t + perm_row(r, 0)) > span) | (key >= kvalid);
+          s[t][r] = kill ? -kInf : s[t][r];  // branch-free select
         }
     }
 
@@ -337,15 +342,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
     if (__builtin_expect(need_mask, false)) {  // boundary tiles only
-      const bool causal = p.causal != 0;
+      // Key j is seen iff my_q - wl <= j <= my_q + hi (hi = 0 under the
+      // causal mask, else the right window edge) and j < kvalid; the band
+      // test is one unsigned compare of j - my_q + wl against wl + hi.
+      const unsigned hi = p.causal ? 0u : (unsigned)p.wr;
+      const unsigned span = (unsigned)p.wl + hi;
+      const unsigned base = (unsigned)(key0 + 8 * hh + p.wl) - (unsigned)my_q;
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * t + perm_row(r, hh);
-          const bool kill = (causal & (key > my_q)) | (key >= kvalid) |  // branch-free select
-                            (key < my_q - p.wl) | (key > my_q + p.wr);
-          s[t][r] = kill ? -kInf : s[t][r];
+          const bool kill =
+              (base + (unsigned)(32 * t + perm_row(r, 0)) > span) | (key >= kvalid);
+          s[t][r] = kill ? -kInf : s[t][r];  // branch-free select
         }
     }
     float mx = tree_max16(s[0]);

@@ -185,6 +185,15 @@ __device__ __forceinline__ void dma_tile(Rsrc rs, const int* voff, uint32_t soff
 // This wave's DMA loads have landed in LDS.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Lane index of a wave64, computed by an opaque mbcnt pair: the compiler
+// cannot hoist or share it, so values derived from it in a loop are rebuilt
+// there instead of being kept live (or spilled) across iterations.
+__device__ __forceinline__ int fresh_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // 16-byte row operand at byte offset `off` of an LDS tile.
 __device__ __forceinline__ bf16x8 lds_row(const char* tile, int off) {
   return *reinterpret_cast<const bf16x8*>(tile + off);
