@@ -14,3 +14,4 @@ from .attention import (  # noqa: F401
     mask_for,
     probabilities,
 )
+from .philox import Dropout, keep_threshold, philox4x32  # noqa: F401

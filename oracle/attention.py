@@ -47,6 +47,17 @@ Masks (all boolean, combined with AND):
   this two-sided band is the plain reading (right = 0 with causal is the
   usual causal local attention).
 
+Dropout (optional): with keep mask Z of one head (``oracle.philox``) and
+realised keep probability q, the forward is O = (P o Z / q) V with P the
+undropped softmax (its LSE unchanged), and the backward differentiates that:
+      dV_j  = sum_i (P_ij Z_ij / q) dO_i
+      dP_ij = (Z_ij / q) dO_i . v_j
+      D_i   = sum_j P_ij dP_ij        (= dO_i . O_i)
+      dS_ij = P_ij (dP_ij - D_i),  dQ and dK as above.
+The zako-mio report (section 3.2) places dropout inside the fused kernel,
+applied on chip and regenerated rather than stored; where it enters (on the
+normalised probabilities, before the product with V) is the standard reading.
+
 Everything is float64; inputs are the exact values the GPU sees, widened.
 """
 from __future__ import annotations
@@ -55,6 +66,8 @@ import dataclasses
 from typing import Optional, Sequence, Tuple
 
 import numpy as np
+
+from .philox import Dropout, HeadDropout
 
 ROW_CHUNK = 128  # rows of S materialised at once (softmax is row-independent)
 
@@ -133,10 +146,12 @@ def probabilities(q: np.ndarray, k: np.ndarray, scale: float, mask: MaskSpec,
 
 
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                 mask: MaskSpec, rows: Optional[Sequence[int]] = None):
+                 mask: MaskSpec, rows: Optional[Sequence[int]] = None,
+                 drop: Optional[HeadDropout] = None):
     """Algorithm-0 forward of one head for the given query rows.
 
     q: [N, d] (only ``rows`` are read), k, v: [N, d]. Returns (O[rows], LSE[rows]).
+    With ``drop``, O = (P o Z / q) V and LSE is that of the undropped P.
     """
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.zeros((len(rows), v.shape[1]))
@@ -145,6 +160,8 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     for rc in _chunks(rows):
         s = _scores(q[rc], k, scale, mask, rc)  # S = Q K^T (materialised)
         p, l = _softmax_rows(s)                  # P = softmax(S)
+        if drop is not None:                     # P <- P o Z / q
+            p = p * (drop.keep(rc, np.arange(k.shape[0])) * drop.scale)
         o[at:at + len(rc)] = p @ v               # O = P V
         lse[at:at + len(rc)] = l
         at += len(rc)
@@ -154,7 +171,8 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                   scale: float, mask: MaskSpec,
                   q_rows: Optional[Sequence[int]] = None,
-                  k_rows: Optional[Sequence[int]] = None):
+                  k_rows: Optional[Sequence[int]] = None,
+                  drop: Optional[HeadDropout] = None):
     """Analytic backward of one query head.
 
     Returns (dQ[q_rows], dK[k_rows], dV[k_rows]) where dK/dV hold this head's
@@ -177,9 +195,14 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
         s = _scores(q[rc], k, scale, mask, rc)
         p, _ = _softmax_rows(s)
         dp = do[rc] @ v.T                                  # dP = dO V^T
+        pv = p                                             # what multiplies V
+        if drop is not None:
+            z = drop.keep(rc, np.arange(n)) * drop.scale   # Z / q
+            pv = p * z
+            dp = dp * z                                    # dP = (Z / q) o dO V^T
         dsum = (p * dp).sum(axis=1)                        # D_i = sum_j P dP
         ds = p * (dp - dsum[:, None])                      # dS = P (dP - D)
-        return p, ds
+        return pv, ds
 
     if want_q is not None:
         at = 0
@@ -198,7 +221,8 @@ def head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
 
 
 def attention_forward(q, k, v, scale, *, causal=False, seqlens=None,
-                      block_mask=None, mask_block=128, window=None):
+                      block_mask=None, mask_block=128, window=None,
+                      dropout: Optional[Dropout] = None):
     """Whole-tensor forward. q: [B, Hq, N, d], k/v: [B, Hkv, N, d] (float64).
 
     Returns O [B, Hq, N, d] and LSE [B, Hq, N].
@@ -211,8 +235,9 @@ def attention_forward(q, k, v, scale, *, causal=False, seqlens=None,
         m = mask_for(b, causal=causal, seqlens=seqlens, block_mask=block_mask,
                      mask_block=mask_block, window=window)
         for h in range(Hq):
-            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h // G], v[b, h // G],
-                                              scale, m)
+            o[b, h], lse[b, h] = head_forward(
+                q[b, h], k[b, h // G], v[b, h // G], scale, m,
+                drop=None if dropout is None else dropout.head(b * Hq + h))
     return o, lse
 
 
@@ -239,7 +264,8 @@ def attention_decode(q, k, v, scale, *, seqlens=None):
 
 
 def attention_backward(q, k, v, do, scale, *, causal=False, seqlens=None,
-                       block_mask=None, mask_block=128, window=None):
+                       block_mask=None, mask_block=128, window=None,
+                       dropout: Optional[Dropout] = None):
     """Whole-tensor backward. Returns dQ [B,Hq,N,d], dK, dV [B,Hkv,N,d]."""
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -252,7 +278,9 @@ def attention_backward(q, k, v, do, scale, *, causal=False, seqlens=None,
                      mask_block=mask_block, window=window)
         for h in range(Hq):
             g = h // G
-            a, bk, bv = head_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, m)
+            a, bk, bv = head_backward(
+                q[b, h], k[b, g], v[b, g], do[b, h], scale, m,
+                drop=None if dropout is None else dropout.head(b * Hq + h))
             dq[b, h] = a
             dk[b, g] += bk
             dv[b, g] += bv

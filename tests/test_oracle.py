@@ -482,12 +482,12 @@ def test_mutants_are_caught(mutant, monkeypatch):
     elif mutant == "dq_scale":
         orig = OA.head_backward
 
-        def hb(q, k, v, do, scale, mask, q_rows=None, k_rows=None):
+        def hb(q, k, v, do, scale, mask, q_rows=None, k_rows=None, drop=None):
             dq, dk, dv = orig(q, k, v, do, scale, mask, q_rows, k_rows)
             return (None if dq is None else dq / scale), dk, dv
         monkeypatch.setattr(OA, "head_backward", hb)
     elif mutant == "ds_no_d":
-        def hb(q, k, v, do, scale, mask, q_rows=None, k_rows=None):
+        def hb(q, k, v, do, scale, mask, q_rows=None, k_rows=None, drop=None):
             # dS = P * dP: the -D_i term dropped.
             p = OA.probabilities(q, k, scale, mask)
             dp = do @ v.T
