@@ -57,17 +57,21 @@ def _strides(t: torch.Tensor) -> Strides:
 
 def make_params(*, dtype=FA_BF16, o_dtype=None, batch, heads_q, heads_kv, seqlen, head_dim,
                 scale=None, causal=False, seqlens_k=0, block_mask=0, block_mask_ld=0,
-                window=None) -> Params:
+                window=None, dropout_p=0.0, dropout_seed=0, dropout_offset=0) -> Params:
     """fa_params from plain values (device pointers as ints); ``window`` is
-    None or a (left, right) sliding-window band."""
+    None or a (left, right) sliding-window band; ``dropout_p`` (stored as
+    float32), ``dropout_seed`` (uint64) and ``dropout_offset`` (uint32) select
+    the in-kernel dropout."""
     wl, wr = (0, 0) if window is None else (int(window[0]), int(window[1]))
     return Params(dtype, dtype if o_dtype is None else o_dtype, batch, heads_q, heads_kv, seqlen,
                   head_dim, 1.0 / math.sqrt(head_dim) if scale is None else scale, int(bool(causal)),
                   seqlens_k or None, block_mask or None, block_mask_ld,
-                  int(window is not None), wl, wr)
+                  int(window is not None), wl, wr, float(dropout_p), int(dropout_offset),
+                  int(dropout_seed))
 
 
-def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype, window) -> Params:
+def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype, window,
+                 dropout_p=0.0, dropout_seed=0, dropout_offset=0) -> Params:
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if k.dtype != q.dtype:
@@ -90,7 +94,9 @@ def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype, window)
     odt = _DT[q.dtype] if o_dtype is None else _DT[o_dtype]
     return make_params(dtype=_DT[q.dtype], o_dtype=odt, batch=B, heads_q=Hq, heads_kv=k.shape[1],
                        seqlen=N, head_dim=d, scale=scale, causal=causal, seqlens_k=sl_ptr,
-                       block_mask=bm_ptr, block_mask_ld=bm_ld, window=window)
+                       block_mask=bm_ptr, block_mask_ld=bm_ld, window=window,
+                       dropout_p=dropout_p, dropout_seed=dropout_seed,
+                       dropout_offset=dropout_offset)
 
 
 def _stream() -> ctypes.c_void_p:
@@ -113,11 +119,14 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
            causal: bool = False, seqlens_k: Optional[torch.Tensor] = None,
            block_mask: Optional[torch.Tensor] = None, o_dtype: Optional[torch.dtype] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           tile_log: bool = False, window: Optional[tuple] = None):
+           tile_log: bool = False, window: Optional[tuple] = None, dropout_p: float = 0.0,
+           dropout_seed: int = 0, dropout_offset: int = 0):
     """Forward pass. Returns (O, LSE, tile_log or None)."""
     lib = _abi.load()
     p = _params_from(q, k, scale=scale, causal=causal, seqlens_k=seqlens_k,
-                     block_mask=block_mask, o_dtype=o_dtype, window=window)
+                     block_mask=block_mask, o_dtype=o_dtype, window=window,
+                     dropout_p=dropout_p, dropout_seed=dropout_seed,
+                     dropout_offset=dropout_offset)
     B, Hq, N, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=o_dtype or q.dtype, device=q.device)
@@ -142,15 +151,19 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
            dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            tile_log: bool = False, stage_events: Optional[Sequence] = None,
-           window: Optional[tuple] = None):
+           window: Optional[tuple] = None, dropout_p: float = 0.0, dropout_seed: int = 0,
+           dropout_offset: int = 0):
     """Backward pass. Returns (dQ, dK, dV, tile_log or None).
 
     ``stage_events``: optional 4 ``torch.cuda.Event`` objects, recorded by
-    the library around its three kernels (for per-kernel timing).
+    the library around its three kernels (for per-kernel timing). The
+    dropout arguments must be those of the forward that produced ``o``.
     """
     lib = _abi.load()
     p = _params_from(q, k, scale=scale, causal=causal, seqlens_k=seqlens_k,
-                     block_mask=block_mask, o_dtype=o.dtype, window=window)
+                     block_mask=block_mask, o_dtype=o.dtype, window=window,
+                     dropout_p=dropout_p, dropout_seed=dropout_seed,
+                     dropout_offset=dropout_offset)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

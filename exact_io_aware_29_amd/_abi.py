@@ -18,9 +18,10 @@ FA_ERR_WORKSPACE = -8
 FA_ERR_HIP = -9
 FA_ERR_MASK = -10
 FA_ERR_SCALE = -11
+FA_ERR_DROPOUT = -12
 STATUS_CODES = [FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE, FA_ERR_HEADDIM, FA_ERR_GQA,
                 FA_ERR_STRIDE, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_MASK,
-                FA_ERR_SCALE]
+                FA_ERR_SCALE, FA_ERR_DROPOUT]
 
 FA_BF16 = 0
 FA_FP32 = 1
@@ -48,6 +49,9 @@ class Params(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
+        ("dropout_p", ctypes.c_float),
+        ("dropout_offset", ctypes.c_uint32),
+        ("dropout_seed", ctypes.c_uint64),
     ]
 
 

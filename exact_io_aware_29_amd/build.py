@@ -28,17 +28,20 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # the kernels never produce NaN from valid input; this lets fmaxf lower
-    # to a bare v_max_f32 (infinities keep their IEEE meaning)
-    "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function",
 ]
 
 
+# Kernel sources only: the kernels never produce NaN from valid input, which
+# lets fmaxf lower to a bare v_max_f32 (infinities keep their IEEE meaning).
+# The host-side API validates user floats and must see NaN as NaN.
+KERNEL_FLAGS = ["-fno-honor-nans"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    lang = ["-x", "hip", *KERNEL_FLAGS] if src.endswith(".hip") else []
     cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -31,6 +31,11 @@ size_t elem_size(int dtype) { return dtype == FA_BF16 ? 2 : 4; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Keep threshold T = round((1 - p) * 65536) (ties away from zero), in double.
+int64_t keep_threshold(float p) {
+  return (int64_t)std::floor((1.0 - (double)p) * 65536.0 + 0.5);
+}
+
 int check_params(const fa_params* p) {
   if (!p) return fail(FA_ERR_NULL, "params is NULL");
   if (p->dtype != FA_BF16 && p->dtype != FA_FP32)
@@ -55,6 +60,10 @@ int check_params(const fa_params* p) {
   if (p->window && (p->window_left < 0 || p->window_right < 0))
     return fail(FA_ERR_MASK, "window widths must be >= 0 (got %d, %d)", p->window_left,
                 p->window_right);
+  if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f))
+    return fail(FA_ERR_DROPOUT, "dropout_p must lie in [0, 1) (got %g)", (double)p->dropout_p);
+  if (p->dropout_p > 0.f && keep_threshold(p->dropout_p) <= 0)
+    return fail(FA_ERR_DROPOUT, "dropout_p %g drops every element", (double)p->dropout_p);
   if (p->block_mask && p->block_mask_ld < blocks)
     return fail(FA_ERR_MASK, "block_mask_ld %d < ceil(seqlen/128) = %lld", p->block_mask_ld,
                 (long long)blocks);
@@ -90,6 +99,15 @@ fa::Problem make_problem(const fa_params* p) {
   // every key, and the kernels apply it unconditionally.
   pr.wl = p->window ? (int)std::min<int64_t>(p->window_left, p->seqlen) : p->seqlen;
   pr.wr = p->window ? (int)std::min<int64_t>(p->window_right, p->seqlen) : p->seqlen;
+  // T = 65536 keeps every element with scale 1: that is no dropout.
+  const int64_t thr = p->dropout_p > 0.f ? keep_threshold(p->dropout_p) : 65536;
+  pr.drop = thr < 65536;
+  pr.drop_thr = (uint32_t)std::min<int64_t>(thr, 65535);
+  pr.drop_scale = (float)(65536.0 / (double)thr);
+  pr.drop_q = (float)((double)thr / 65536.0);
+  pr.seed_lo = (uint32_t)(p->dropout_seed & 0xFFFFFFFFu);
+  pr.seed_hi = (uint32_t)(p->dropout_seed >> 32);
+  pr.drop_off = p->dropout_offset;
   return pr;
 }
 
@@ -253,6 +271,7 @@ int check_decode_params(const fa_params* p) {
   if (p->dtype != FA_BF16) return fail(FA_ERR_DTYPE, "decode supports bf16 inputs only");
   if (p->block_mask) return fail(FA_ERR_MASK, "decode takes no block mask");
   if (p->window) return fail(FA_ERR_MASK, "decode takes no sliding window");
+  if (p->dropout_p != 0.f) return fail(FA_ERR_DROPOUT, "decode takes no dropout");
   return FA_OK;
 }
 
@@ -320,6 +339,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_MASK: return "block_mask_ld smaller than the number of 128-key blocks";
     case FA_ERR_SCALE: return "scale must be finite and positive";
+    case FA_ERR_DROPOUT: return "dropout_p outside [0, 1) or too close to 1";
     default: return "unknown status";
   }
 }

@@ -19,6 +19,7 @@
 // computing it from the stored O costs one pass over O and dO instead of a
 // second reduction per tile. All gradients stay in fp32 registers for the
 // whole key (or query) block and are written once; there are no atomics.
+#include "fa_philox.h"
 #include "fa_stage.h"
 
 namespace fa {
@@ -69,7 +70,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (part == 0 && row < rows) {
-    a.dvec[row] = acc;
+    // Under dropout the kernels use q D (q the keep probability): with
+    // dP = (Z / q) o dO V^T, dS = P o (dP - D) = (1 / q) P o (Z o dO V^T - q D),
+    // and the 1 / q joins the final scale of dQ and dK.
+    a.dvec[row] = a.p.drop ? acc * a.p.drop_q : acc;
     a.lse2[row] = lse2_of(a.lse[row]);
   }
 }
@@ -105,7 +109,7 @@ struct DkdvCfg {
   static_assert(STAGE % 256 == 0, "stages keep the 256-byte bank period");
 };
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<D>;
   using T = typename C::T;
@@ -319,8 +323,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
           const f32x4* d4 =
               reinterpret_cast<const f32x4*>(Qs + C::DVEC_OFF) + 8 * (g0 + uu) + 2 * hh;
           const f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
+          if constexpr (DROP) {
+            // Keep bits of this lane's key for the sub-tile's 16 rows: the 8
+            // lanes that share a key group (lane % 8 = key % 8) each run the
+            // generator for two of the rows (rows perm_row(e, hh) and
+            // perm_row(8 + e, hh), e = lane % 8) and a bit transpose across
+            // those lanes hands every lane bit r = row perm_row(r, hh).
+            const int ln = fresh_lane_id();
+            const int e = ln & 7, hl = ln >> 5;
+            const uint32_t kg = (uint32_t)(k0 + 32 * w + (ln & 24)) >> 3;
+            const uint32_t row0 = (uint32_t)(q0b + 32 * (g0 + uu) + 8 * hl + e);
+            const uint32_t bh = (uint32_t)(b * p.Hq + h);
+            const uint32_t lo = drop_byte(drop_bits(p, kg, row0, bh), p.drop_thr);
+            const uint32_t hi = drop_byte(drop_bits(p, kg, row0 + 16, bh), p.drop_thr);
+            const uint32_t bits = transpose8x8x2(lo | (hi << 8));
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * (dp[uu][r] - dv4[r >> 2][r & 3]);
+            for (int r = 0; r < 16; ++r) {
+              const bool keep = (bits >> r) & 1u;
+              // dS' = P (Z dP~ - q D) (the D row vector holds q D); P o Z for dV
+              dp[uu][r] = s[uu][r] * ((keep ? dp[uu][r] : 0.f) - dv4[r >> 2][r & 3]);
+              s[uu][r] = keep ? s[uu][r] : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * (dp[uu][r] - dv4[r >> 2][r & 3]);
+          }
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const bf16x8 pf = pack8(s[uu], c);
@@ -344,6 +371,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       step(smem + st * C::STAGE, smem + (st ^ 1) * C::STAGE, smem + C::VOFF);
   }
 
+  // Under dropout both products carry the 1 / q of the kept probabilities.
+  const float vscale = DROP ? p.drop_scale : 1.f;
+  const float kscale = p.scale * vscale;
   if (my_k < p.N) {
     bf16* dkp = static_cast<bf16*>(a.dk) + b * a.sdk.b + hk * a.sdk.h + (int64_t)my_k * a.sdk.n;
     bf16* dvp = static_cast<bf16*>(a.dv) + b * a.sdv.b + hk * a.sdv.h + (int64_t)my_k * a.sdv.n;
@@ -355,8 +385,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         bf16x4 kq, vq;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kq[e] = (bf16)(dkt[db][4 * g + e] * p.scale);
-          vq[e] = (bf16)dvt[db][4 * g + e];
+          kq[e] = (bf16)(dkt[db][4 * g + e] * kscale);
+          vq[e] = (bf16)(dvt[db][4 * g + e] * vscale);
         }
         *reinterpret_cast<bf16x4*>(dkp + d0) = kq;
         *reinterpret_cast<bf16x4*>(dvp + d0) = vq;
@@ -376,7 +406,7 @@ struct DqCfg {
   using T = SwzTile<D, BC>;
 };
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D>;
   using T = typename C::T;
@@ -497,6 +527,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           st[r] = kill ? 0.f : st[r];  // branch-free select
         }
       }
+      if constexpr (DROP) {  // dP~ of dropped entries is zero (dq_d holds q D)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          drop_run8(dpt, 8 * c,
+                    drop_bits(p, (uint32_t)(key0 + 32 * t + 16 * c + 8 * hh) >> 3,
+                              (uint32_t)my_q, (uint32_t)(b * p.Hq + h)),
+                    p.drop_thr);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (dpt[r] - dq_d);
 #pragma unroll
@@ -516,6 +554,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
 
+  const float qscale = DROP ? p.scale * p.drop_scale : p.scale;
   if (qok) {
     bf16* dqp = static_cast<bf16*>(a.dq) + b * a.sdq.b + h * a.sdq.h + (int64_t)my_q * a.sdq.n;
 #pragma unroll
@@ -524,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[db][4 * g + e] * p.scale);
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[db][4 * g + e] * qscale);
         *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * g + 4 * hh) = v;
       }
   }
@@ -545,19 +584,27 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t s) {
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t grid = (int64_t)((a.p.N + 127) / 128) * a.p.Hkv * a.p.B;
-  if (head_dim == 64)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  const dim3 g((unsigned)grid), blk(256);
+  if (head_dim == 64) {
+    if (a.p.drop) hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), g, blk, 0, s, a);
+  } else {
+    if (a.p.drop) hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), g, blk, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t grid = (int64_t)((a.p.N + 127) / 128) * a.p.Hq * a.p.B;
-  if (head_dim == 64)
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  const dim3 g((unsigned)grid), blk(256);
+  if (head_dim == 64) {
+    if (a.p.drop) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<64, false>), g, blk, 0, s, a);
+  } else {
+    if (a.p.drop) hipLaunchKernelGGL((bwd_dq_kernel<128, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), g, blk, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -22,6 +22,13 @@
 // Tiles with no allowed entry (causal upper triangle, keys past the valid
 // length, absent block-mask blocks) are skipped before they are loaded;
 // element masks are applied only on tiles that straddle a boundary.
+//
+// Dropout (zako-mio report, section 3.2: part of the fused kernel): after
+// P~ has entered the row sum, dropped entries are zeroed before the PV
+// product, and the final 1 / l also carries the 1 / q rescale. Each lane
+// regenerates its row's keep bits with one Philox call per run of 8
+// consecutive keys it holds; nothing is stored.
+#include "fa_philox.h"
 #include "fa_stage.h"
 
 namespace fa {
@@ -150,6 +157,16 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    if (p.drop) {  // register r of sub-tile t is key key0 + 32 t + perm_row(r, hh)
+#pragma unroll
+      for (int t = 0; t < C::NSUB; ++t)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          drop_run8(s[t], 8 * c,
+                    drop_bits(p, (uint32_t)(key0 + 32 * t + 16 * c + 8 * hh) >> 3,
+                              (uint32_t)my_q, (uint32_t)(b * p.Hq + h)),
+                    p.drop_thr);
+    }
 
     // O^T += V^T P~^T: the P~ registers are the B operand directly.
 #pragma unroll
@@ -177,9 +194,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  // Epilogue: O = O~ / l, LSE = m * scale + ln l (natural log).
+  // Epilogue: O = O~ / l (times 1 / q under dropout), LSE = m * scale + ln l.
   const float l_tot = half_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (p.drop ? p.drop_scale : 1.f) / l_tot : 0.f;
   if (my_q < p.N) {
     char* obase = static_cast<char*>(a.o);
     const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n;
@@ -225,7 +242,7 @@ struct FwdB {
   static constexpr float kLag = 8.f;
 };
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   using C = FwdB<D>;
   using T = typename C::T;
@@ -378,6 +395,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, -m_use));
       l_run += tree_sum16(s[t]);
+      if constexpr (DROP) {  // zero dropped entries after they entered l
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          drop_run8(s[t], 8 * c,
+                    drop_bits(p, (uint32_t)(key0 + 32 * t + 16 * c + 8 * hh) >> 3,
+                              (uint32_t)my_q, (uint32_t)(b * p.Hq + h)),
+                    p.drop_thr);
+      }
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -409,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
 
   const float l_tot = half_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;
   if (my_q < p.N) {
     char* obase = static_cast<char*>(a.o);
     const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n;
@@ -451,7 +476,10 @@ template <int D>
 static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const int64_t nqb = (a.p.N + FwdB<D>::BR - 1) / FwdB<D>::BR;
   const int64_t grid = nqb * a.p.Hq * a.p.B;
-  hipLaunchKernelGGL((fwd_kernel_bf16<D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  if (a.p.drop)
+    hipLaunchKernelGGL((fwd_kernel_bf16<D, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel_bf16<D, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -23,6 +23,13 @@ struct Problem {
   int logw;  // uint32 words per tile-log row: ceil(nlb / 32)
   int wl, wr;  // sliding window: key j allowed for query i iff i - wl <= j <= i + wr
                // (both in [0, N]; N when there is no window)
+  // Dropout (drop != 0): element kept iff its 16-bit Philox uniform is below
+  // drop_thr (1 .. 65535); kept probabilities are scaled by drop_scale =
+  // 65536 / drop_thr, and drop_q = drop_thr / 65536 is the keep probability.
+  int drop;
+  uint32_t drop_thr;
+  float drop_scale, drop_q;
+  uint32_t seed_lo, seed_hi, drop_off;
 };
 
 struct FwdArgs {

@@ -72,7 +72,8 @@ enum fa_status {
   FA_ERR_WORKSPACE = -8, /* workspace missing or smaller than required */
   FA_ERR_HIP = -9,       /* a HIP call failed (see fa_last_error_detail) */
   FA_ERR_MASK = -10,     /* block_mask_ld smaller than ceil(seqlen / 128) */
-  FA_ERR_SCALE = -11     /* scale is not finite and positive */
+  FA_ERR_SCALE = -11,    /* scale is not finite and positive */
+  FA_ERR_DROPOUT = -12   /* dropout_p outside [0, 1) or too close to 1 */
 };
 
 /* Element types. */
@@ -116,6 +117,23 @@ typedef struct fa_params {
   int32_t window;
   int32_t window_left;
   int32_t window_right;
+  /* Dropout on the attention probabilities, applied on chip and regenerated
+   * by every kernel that needs it, never stored (the zako-mio report,
+   * section 3.2, fuses dropout into the single attention kernel). With
+   * 0 < dropout_p < 1, element (b, h, i, j) draws the 16-bit uniform
+   *   u = half (j mod 2) [0 = low 16 bits] of word ((j div 2) mod 4) of
+   *       Philox4x32-10(counter = (j div 8, i, b * heads_q + h, dropout_offset),
+   *                     key = (dropout_seed mod 2^32, dropout_seed div 2^32))
+   * (Salmon et al., SC'11) and is kept iff u < T, T = round((1 - p) 65536)
+   * in double precision; kept probabilities are scaled by 65536 / T.
+   * O = (P o Z * 65536 / T) V with P the undropped softmax, so LSE is
+   * unchanged; fa_bwd regenerates the same mask from the same fields.
+   * dropout_p = 0 (a zero-initialised struct) means no dropout; p outside
+   * [0, 1), or so close to 1 that T = 0, is FA_ERR_DROPOUT. fa_decode
+   * accepts dropout_p = 0 only. */
+  float dropout_p;
+  uint32_t dropout_offset;
+  uint64_t dropout_seed;
 } fa_params;
 
 /*

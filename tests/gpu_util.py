@@ -98,11 +98,12 @@ def decode_log(words: torch.Tensor, B, Hq, N) -> np.ndarray:
     return bits
 
 
-def oracle_heads(inp, heads, *, backward=True, q_rows=None, k_rows=None):
+def oracle_heads(inp, heads, *, backward=True, q_rows=None, k_rows=None, dropout=None):
     """Oracle results for selected (b, h) query heads.
 
     Returns dict (b, h) -> dict(o, lse, dq) for q_rows (all rows if None),
     and (b, g) -> dict(dk, dv) summed over the whole GQA group for k_rows.
+    ``dropout`` is an ``oracle.Dropout`` applied to every head.
     """
     w = inp.workload
     G = w.heads_q // w.heads_kv
@@ -115,12 +116,14 @@ def oracle_heads(inp, heads, *, backward=True, q_rows=None, k_rows=None):
         q = inp.as_f64("q", (b, h))
         k = inp.as_f64("k", (b, g))
         v = inp.as_f64("v", (b, g))
-        o, lse = oracle.head_forward(q, k, v, inp.scale, m, rows=q_rows)
+        drop = None if dropout is None else dropout.head(b * w.heads_q + h)
+        o, lse = oracle.head_forward(q, k, v, inp.scale, m, rows=q_rows, drop=drop)
         ent = dict(o=o, lse=lse)
         if backward:
             do = inp.as_f64("do", (b, h))
             dq, _, _ = oracle.head_backward(q, k, v, do, inp.scale, m,
-                                            q_rows=np.arange(w.seqlen) if q_rows is None else q_rows)
+                                            q_rows=np.arange(w.seqlen) if q_rows is None else q_rows,
+                                            drop=drop)
             ent["dq"] = dq
             if (b, g) not in kv_done:
                 kv_done.add((b, g))
@@ -130,7 +133,9 @@ def oracle_heads(inp, heads, *, backward=True, q_rows=None, k_rows=None):
                 for hh in range(g * G, (g + 1) * G):
                     qh = inp.as_f64("q", (b, hh))
                     doh = inp.as_f64("do", (b, hh))
-                    _, a, c = oracle.head_backward(qh, k, v, doh, inp.scale, m, k_rows=kr)
+                    dh = None if dropout is None else dropout.head(b * w.heads_q + hh)
+                    _, a, c = oracle.head_backward(qh, k, v, doh, inp.scale, m, k_rows=kr,
+                                                   drop=dh)
                     dk += a
                     dv += c
                 res[(b, g, "kv")] = dict(dk=dk, dv=dv)

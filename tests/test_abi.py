@@ -51,7 +51,8 @@ def test_status_codes_match_header():
     codes = dict((n, int(v)) for n, v in re.findall(r"(FA_\w+)\s*=\s*(-?\d+)", text))
     for name in ("FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_DTYPE", "FA_ERR_HEADDIM",
                  "FA_ERR_GQA", "FA_ERR_STRIDE", "FA_ERR_ALIGN", "FA_ERR_WORKSPACE",
-                 "FA_ERR_HIP", "FA_ERR_MASK", "FA_ERR_SCALE", "FA_BF16", "FA_FP32"):
+                 "FA_ERR_HIP", "FA_ERR_MASK", "FA_ERR_SCALE", "FA_ERR_DROPOUT", "FA_BF16",
+                 "FA_FP32"):
         assert codes[name] == getattr(_abi, name), name
     msgs = {fa.fa_strerror(c) for c in _abi.STATUS_CODES}
     assert len(msgs) == len(_abi.STATUS_CODES)
@@ -99,6 +100,10 @@ def _fwd(p, q=P16, k=P32, v=P48, o=P64, lse=P80, sq=None, sk=None, so=None, log=
     (dict(block_mask=0x9000, block_mask_ld=2), _abi.FA_ERR_MASK),
     (dict(window=(-1, 4)), _abi.FA_ERR_MASK),
     (dict(window=(3, -2)), _abi.FA_ERR_MASK),
+    (dict(dropout_p=1.0), _abi.FA_ERR_DROPOUT),
+    (dict(dropout_p=-0.1), _abi.FA_ERR_DROPOUT),
+    (dict(dropout_p=math.nan), _abi.FA_ERR_DROPOUT),
+    (dict(dropout_p=0.999995), _abi.FA_ERR_DROPOUT),  # T = round(0.33) = 0
     (dict(batch=1 << 20, heads_q=1 << 10, heads_kv=1 << 10, seqlen=1 << 20), _abi.FA_ERR_SHAPE),
 ])
 def test_fwd_rejects_bad_params(mut, code):
@@ -165,3 +170,52 @@ def test_params_struct_window_fields():
     p = _params(window=(12, 0))
     assert (p.window, p.window_left, p.window_right) == (1, 12, 0)
     assert _params().window == 0
+
+
+def test_params_struct_dropout_fields():
+    """A zero-initialised fa_params has no dropout; make_params stores p as
+    float32, the 64-bit seed and the 32-bit offset."""
+    z = _abi.Params()
+    assert z.dropout_p == 0.0 and z.dropout_seed == 0 and z.dropout_offset == 0
+    p = _params(dropout_p=0.1, dropout_seed=2**64 - 1, dropout_offset=2**32 - 1)
+    assert p.dropout_p == ctypes.c_float(0.1).value
+    assert (p.dropout_seed, p.dropout_offset) == (2**64 - 1, 2**32 - 1)
+
+
+def test_struct_layout_matches_the_c_header(tmp_path):
+    """Field offsets and sizes of the ctypes mirrors equal those the C
+    compiler gives include/fa.h."""
+    import subprocess
+    fields = [f for f, _ in _abi.Params._fields_]
+    src = ['#include <stddef.h>', '#include <stdio.h>', '#include "fa.h"', "int main(void) {",
+           '  printf("%zu\\n", sizeof(fa_params));',
+           '  printf("%zu\\n", sizeof(fa_strides));']
+    src += [f'  printf("%zu\\n", offsetof(fa_params, {f}));' for f in fields]
+    src += ["  return 0;", "}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)],
+                   check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(_abi.Params)
+    assert vals[1] == ctypes.sizeof(_abi.Strides)
+    for f, off in zip(fields, vals[2:]):
+        assert getattr(_abi.Params, f).offset == off, f
+
+
+@no_gpu_only
+def test_decode_rejects_dropout_window_and_mask():
+    lib = fa.library()
+
+    def call(**kw):
+        p = _params(heads_q=8, heads_kv=2, **kw)
+        sq = _abi.Strides(8 * 64, 64, 64)
+        skv = _strides(p, p.heads_kv)
+        st = lib.fa_decode(ctypes.byref(p), P16, sq, P32, skv, P48, skv, P64, sq, P80,
+                           ctypes.c_void_p(0x7000), 1 << 30, None)
+        return st
+    assert call(dropout_p=0.1) == _abi.FA_ERR_DROPOUT
+    assert call(window=(4, 0)) == _abi.FA_ERR_MASK
+    assert call(dtype=_abi.FA_FP32, o_dtype=_abi.FA_FP32) == _abi.FA_ERR_DTYPE
