@@ -30,9 +30,9 @@ DECODE_METRIC = ("decode attention KV-cache read GB/s (one query row per head), 
 KERNEL_SOURCES = {
     "decode": ["fa_decode.hip", "fa_stage.h", "fa_device.h"],
     "decode_combine": ["fa_decode.hip"],
-    "fwd": ["fa_fwd.hip", "fa_stage.h", "fa_device.h"],
-    "bwd_dkdv": ["fa_bwd.hip", "fa_stage.h", "fa_device.h"],
-    "bwd_dq": ["fa_bwd.hip", "fa_stage.h", "fa_device.h"],
+    "fwd": ["fa_fwd.hip", "fa_stage.h", "fa_device.h", "fa_philox.h"],
+    "bwd_dkdv": ["fa_bwd.hip", "fa_stage.h", "fa_device.h", "fa_philox.h"],
+    "bwd_dq": ["fa_bwd.hip", "fa_stage.h", "fa_device.h", "fa_philox.h"],
     "bwd_pre": ["fa_bwd.hip"],
 }
 
@@ -89,6 +89,8 @@ def cpu_baseline(inp, pairs_per_head, budget_s):
         cores = 1
     w = inp.workload
     G = w.heads_q // w.heads_kv
+    dr = None if w.dropout is None else oracle.Dropout(float(np.float32(w.dropout[0])),
+                                                       w.dropout[1], w.dropout[2])
     done, flop = 0, 0
     t0 = time.perf_counter()
     for b in range(w.batch):
@@ -98,9 +100,10 @@ def cpu_baseline(inp, pairs_per_head, budget_s):
             q = inp.as_f64("q", (b, h))
             k = inp.as_f64("k", (b, h // G))
             v = inp.as_f64("v", (b, h // G))
-            oracle.head_forward(q, k, v, inp.scale, m)
+            drop = None if dr is None else dr.head(b * w.heads_q + h)
+            oracle.head_forward(q, k, v, inp.scale, m, drop=drop)
             if w.backward:
-                oracle.head_backward(q, k, v, inp.as_f64("do", (b, h)), inp.scale, m)
+                oracle.head_backward(q, k, v, inp.as_f64("do", (b, h)), inp.scale, m, drop=drop)
             done += 1
             flop += (14 if w.backward else 4) * w.head_dim * pairs_per_head[b]
             if time.perf_counter() - t0 >= budget_s:
@@ -276,6 +279,8 @@ def main():
     sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).to(dev)
     bm = None if inp.block_mask is None else torch.from_numpy(inp.block_mask).to(dev)
     kw = dict(scale=inp.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, window=w.window)
+    if w.dropout is not None:
+        kw.update(dropout_p=w.dropout[0], dropout_seed=w.dropout[1], dropout_offset=w.dropout[2])
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     if w.backward:
@@ -364,7 +369,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, rounded to bf16)",
         "config": {"workload": w.describe(), "batch": w.batch, "heads_q": w.heads_q,
                    "heads_kv": w.heads_kv, "seqlen": w.seqlen, "head_dim": w.head_dim,
-                   "causal": w.causal, "pass": "fwd+bwd" if w.backward else "fwd"},
+                   "causal": w.causal, "pass": "fwd+bwd" if w.backward else "fwd",
+                   "dropout_p": 0.0 if w.dropout is None else w.dropout[0]},
         "pct_of_peak_fwd_bwd": round(100 * value / peak, 2),
         "fwd_tflops": round(fwd_tf, 2),
         "pct_of_peak_fwd": round(100 * fwd_tf / peak, 2),

@@ -176,8 +176,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       dma_offsets<D, C::BQ>(dvo, dsb, w, lane);
     }
     static_assert(2 * C::NRC <= 4, "one wave per 64-row statistics load");
-    int roff[C::NKK], troff[C::NDB][2];
-    row_offsets<D, C::BQ>(roff, lr, hh);
+    int roff_k[C::VLDS ? 1 : C::NKK], troff[C::NDB][2];
+    if constexpr (C::VLDS) {
+      // Only step 0's row offset stays live; the others are rebuilt per
+      // step (chunk 2 kk + hh of a swizzled row = step 0's offset XOR 32 kk).
+      roff_k[0] = T::off(swap_bits23(lr), hh);
+    } else {
+      row_offsets<D, C::BQ>(roff_k, lr, hh);
+    }
     tr_offsets<D, C::BQ>(troff, lane);
 
     // Q and dO tiles of a step and the LSE / D values of its rows all arrive
@@ -241,15 +247,44 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       // step kk (chunk 2 kk + hh) is step 0's offset XOR 32 kk; rebuilt each
       // step from one live register (all eight kept live across the loop
       // would push a row offset out to scratch).
-      int vboff[C::VLDS ? C::NKK : 1];
+      int vboff[C::VLDS ? C::NKK : 1], roff[C::NKK];
       if constexpr (C::VLDS) {
-        int v0 = vb0;
-        asm volatile("" : "+v"(v0));
+        int v0 = vb0, r0 = roff_k[0];
+        asm volatile("" : "+v"(v0), "+v"(r0));
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) vboff[kk] = v0 ^ (32 * kk);
+        for (int kk = 0; kk < C::NKK; ++kk) {
+          vboff[kk] = v0 ^ (32 * kk);
+          roff[kk] = r0 ^ (32 * kk);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) roff[kk] = roff_k[kk];
       }
       const int nx = next_step(sidx + 1);
       if (nx < nsteps) issue(nx, fill);  // lands during this step
+      // Dropout keep bits of this lane's key for every row of the step, made
+      // before the score products so that the generator's temporaries never
+      // share the registers with the S and dP accumulators (the empty asm
+      // with a memory clobber keeps the block ahead of the LDS reads). The 8
+      // lanes that share a key group (lane % 8 = key % 8) each run the
+      // generator for two rows of a sub-tile (perm_row(e, hh) and
+      // perm_row(8 + e, hh), e = lane % 8); a bit transpose across those
+      // lanes hands every lane bit r = row perm_row(r, hh).
+      uint32_t dbits[DROP ? C::NQS : 1];
+      if constexpr (DROP) {
+        const int ln = fresh_lane_id();
+        const int e = ln & 7, hl = ln >> 5;
+        const uint32_t kg = (uint32_t)(k0 + 32 * w + (ln & 24)) >> 3;
+        const uint32_t bh = (uint32_t)(b * p.Hq + h);
+#pragma unroll
+        for (int u = 0; u < C::NQS; ++u) {
+          const uint32_t row0 = (uint32_t)(q0b + 32 * u + 8 * hl + e);
+          const uint32_t lo = drop_byte(drop_bits(p, kg, row0, bh), p.drop_thr);
+          const uint32_t hi = drop_byte(drop_bits(p, kg, row0 + 16, bh), p.drop_thr);
+          dbits[u] = transpose8x8x2(lo | (hi << 8));
+          asm volatile("" : "+v"(dbits[u]) : : "memory");
+        }
+      }
       if (a.log_kv && tid == 0)
         log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
       const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid) ||
@@ -324,25 +359,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
               reinterpret_cast<const f32x4*>(Qs + C::DVEC_OFF) + 8 * (g0 + uu) + 2 * hh;
           const f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
           if constexpr (DROP) {
-            // Keep bits of this lane's key for the sub-tile's 16 rows: the 8
-            // lanes that share a key group (lane % 8 = key % 8) each run the
-            // generator for two of the rows (rows perm_row(e, hh) and
-            // perm_row(8 + e, hh), e = lane % 8) and a bit transpose across
-            // those lanes hands every lane bit r = row perm_row(r, hh).
-            const int ln = fresh_lane_id();
-            const int e = ln & 7, hl = ln >> 5;
-            const uint32_t kg = (uint32_t)(k0 + 32 * w + (ln & 24)) >> 3;
-            const uint32_t row0 = (uint32_t)(q0b + 32 * (g0 + uu) + 8 * hl + e);
-            const uint32_t bh = (uint32_t)(b * p.Hq + h);
-            const uint32_t lo = drop_byte(drop_bits(p, kg, row0, bh), p.drop_thr);
-            const uint32_t hi = drop_byte(drop_bits(p, kg, row0 + 16, bh), p.drop_thr);
-            const uint32_t bits = transpose8x8x2(lo | (hi << 8));
+            const uint32_t bits = dbits[g0 + uu];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const bool keep = (bits >> r) & 1u;
-              // dS' = P (Z dP~ - q D) (the D row vector holds q D); P o Z for dV
-              dp[uu][r] = s[uu][r] * ((keep ? dp[uu][r] : 0.f) - dv4[r >> 2][r & 3]);
-              s[uu][r] = keep ? s[uu][r] : 0.f;
+              // All-ones / all-zero mask from keep bit r; P o Z is one AND.
+              int m = __builtin_amdgcn_sbfe((int)bits, r, 1);
+              asm("" : "+v"(m));  // opaque: keeps the AND (not a compare + select)
+              const float pz = __int_as_float(__float_as_int(s[uu][r]) & m);
+              // dS' = P (Z dP~ - q D) = (P o Z) dP~ - P (q D)  (the D row
+              // vector holds q D); P o Z also feeds dV.
+              dp[uu][r] = fmaf(pz, dp[uu][r], -s[uu][r] * dv4[r >> 2][r & 3]);
+              s[uu][r] = pz;
             }
           } else {
 #pragma unroll

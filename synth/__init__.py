@@ -49,6 +49,7 @@ class Workload:
     backward: bool = True
     window: Optional[tuple] = None  # (left, right) sliding-window band
     decode: bool = False  # one query row per head against `seqlen` cached keys
+    dropout: Optional[tuple] = None  # (p, seed, offset) of in-kernel dropout
 
     @property
     def group(self) -> int:
@@ -75,6 +76,8 @@ class Workload:
             parts.append("butterfly128")
         if self.window is not None:
             parts.append(f"window{self.window[0]}-{self.window[1]}")
+        if self.dropout is not None:
+            parts.append(f"dropout{self.dropout[0]}")
         if self.decode:
             parts.append("decode")
             return " ".join(parts)
@@ -99,6 +102,13 @@ WORKLOADS = {
     # [16384, 32768]); the pages fix no such shape.
     7: Workload("decode-32k-gqa", 16, 32, 8, 32768, 128, "bf16", pad_range=(16384, 32768),
                 backward=False, decode=True),
+    # In-kernel dropout (p = 0.1, fixed seed and offset): the headline shape,
+    # and the causal key-padded d = 128 shape -- dropout with a padding mask
+    # is the setting of the pages' memory / runtime comparison.
+    8: Workload("gpt2-medium-attn-dropout", 64, 16, 16, 1024, 64, "bf16",
+                dropout=(0.1, 0x5EED, 0)),
+    9: Workload("causal-keypad-dropout", 8, 16, 16, 4096, 128, "bf16", causal=True,
+                pad_range=(2048, 4096), dropout=(0.1, 0x5EED, 0)),
 }
 
 
