@@ -19,6 +19,11 @@ Recipe (one generator per workload, numpy PCG64 seeded with the workload id):
   instantiated on a 2^k block grid as: block (i, j) is present iff i XOR j has
   at most one bit set (the diagonal plus one partner per bit).
 * The softmax scale is 1/sqrt(head_dim), passed around as a float32 value.
+* fp8 workloads encode each draw x as the OCP e4m3 (E4M3FN) value nearest to
+  x / descale (ties to even mantissa, saturating at +-448) with the
+  workload's per-tensor descale factors; the logical input is then
+  descale * decode(code), which is what the oracle reads. A power-of-two
+  descale keeps that product exact.
 """
 from __future__ import annotations
 
@@ -50,6 +55,7 @@ class Workload:
     window: Optional[tuple] = None  # (left, right) sliding-window band
     decode: bool = False  # one query row per head against `seqlen` cached keys
     dropout: Optional[tuple] = None  # (p, seed, offset) of in-kernel dropout
+    descale: tuple = (1.0, 1.0, 1.0)  # fp8: per-tensor (q, k, v) descale factors
 
     @property
     def group(self) -> int:
@@ -78,6 +84,8 @@ class Workload:
             parts.append(f"window{self.window[0]}-{self.window[1]}")
         if self.dropout is not None:
             parts.append(f"dropout{self.dropout[0]}")
+        if self.dtype == "fp8" and tuple(self.descale) != (1.0, 1.0, 1.0):
+            parts.append("descale" + "/".join(f"{x:g}" for x in self.descale))
         if self.decode:
             parts.append("decode")
             return " ".join(parts)
@@ -109,6 +117,13 @@ WORKLOADS = {
                 dropout=(0.1, 0x5EED, 0)),
     9: Workload("causal-keypad-dropout", 8, 16, 16, 4096, 128, "bf16", causal=True,
                 pad_range=(2048, 4096), dropout=(0.1, 0x5EED, 0)),
+    # FP8 (e4m3) forward: the headline shape and the causal key-padded d = 128
+    # shape, inputs encoded at x * 16 with descale 1/16 (the pages fix no FP8
+    # workload; these reuse the exact-attention shapes).
+    10: Workload("gpt2-medium-attn-fp8", 64, 16, 16, 1024, 64, "fp8", backward=False,
+                 descale=(0.0625, 0.0625, 0.0625)),
+    11: Workload("causal-keypad-fp8", 8, 16, 16, 4096, 128, "fp8", causal=True,
+                 pad_range=(2048, 4096), backward=False, descale=(0.0625, 0.0625, 0.0625)),
 }
 
 
@@ -129,6 +144,42 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Encode values as OCP e4m3 (E4M3FN: 1 sign, 4 exponent bits with bias
+    7, 3 mantissa bits, subnormals below 2^-6, no infinities, NaN = S.1111.111,
+    largest finite 448): the nearest representable value, ties to an even
+    mantissa, magnitudes above 448 saturating to 448. Inputs must be finite.
+    Returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.minimum(np.abs(x), 448.0)
+    # binade exponent, floored at the subnormal range (spacing 2^-9 there)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    quantum = np.exp2(e - 3)
+    q = np.round(a / quantum) * quantum          # numpy rounds half to even
+    q = np.minimum(q, 448.0)
+    # re-derive the exponent of the rounded value (rounding may carry up)
+    qe = np.floor(np.log2(np.where(q > 0, q, 1.0)))
+    normal = q >= 2.0 ** -6
+    E = np.where(normal, qe + 7, 0).astype(np.int64)
+    M = np.where(normal, np.round((q / np.exp2(qe) - 1.0) * 8), np.round(q / 2.0 ** -9))
+    M = M.astype(np.int64)
+    code = (E << 3) | M
+    return (sign | code.astype(np.uint8)).astype(np.uint8)
+
+
+def e4m3_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Decode OCP e4m3 codes exactly (NaN for the two NaN codes)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    s = np.where(b & 0x80, -1.0, 1.0)
+    E = (b >> 3) & 15
+    M = b & 7
+    v = np.where(E == 0, M * 2.0 ** -9, (1.0 + M / 8.0) * np.exp2(E - 7.0))
+    v = np.where((E == 15) & (M == 7), np.nan, v)
+    return s * v
+
+
 def butterfly_block_mask(nblocks: int) -> np.ndarray:
     """uint8 [nblocks, nblocks]: 1 where popcount(i XOR j) <= 1."""
     i = np.arange(nblocks, dtype=np.int64)[:, None]
@@ -143,7 +194,8 @@ class Inputs:
     """One drawn problem. Tensors are in [B, H, N, d] order, C-contiguous.
 
     For bf16 workloads q/k/v/do hold uint16 bit patterns; for fp32 they hold
-    float32 values. ``seqlens`` is int32 [B] or None; ``block_mask`` is uint8
+    float32 values; for fp8 q/k/v hold uint8 e4m3 codes of value / descale.
+    ``seqlens`` is int32 [B] or None; ``block_mask`` is uint8
     [ceil(N/128), ceil(N/128)] or None.
     """
 
@@ -156,14 +208,19 @@ class Inputs:
     block_mask: Optional[np.ndarray]
     scale: float
     window: Optional[tuple] = None
+    descale: tuple = (1.0, 1.0, 1.0)
 
     def as_f64(self, name: str, index=None) -> np.ndarray:
-        """Exact float64 view of tensor ``name`` (optionally sliced first)."""
+        """Exact float64 view of tensor ``name`` (optionally sliced first);
+        for fp8 the logical value descale * decode(code)."""
         a = getattr(self, name)
         if index is not None:
             a = a[index]
         if self.workload.dtype == "bf16":
             return bf16_bits_to_f64(a)
+        if self.workload.dtype == "fp8":
+            ds = dict(q=self.descale[0], k=self.descale[1], v=self.descale[2])[name]
+            return e4m3_bits_to_f64(a) * ds
         return np.asarray(a, dtype=np.float64)
 
 
@@ -174,13 +231,17 @@ def draw(w: Workload, seed: int, *, with_do: Optional[bool] = None) -> Inputs:
     qshape = (w.batch, w.heads_q, 1 if w.decode else w.seqlen, w.head_dim)
     kshape = (w.batch, w.heads_kv, w.seqlen, w.head_dim)
 
-    def one(shape):
+    def one(shape, ds=1.0):
         x = rng.standard_normal(shape, dtype=np.float32)
-        return f32_to_bf16_bits(x) if w.dtype == "bf16" else x
+        if w.dtype == "bf16":
+            return f32_to_bf16_bits(x)
+        if w.dtype == "fp8":
+            return f32_to_e4m3_bits(x.astype(np.float64) / ds)
+        return x
 
-    q = one(qshape)
-    k = one(kshape)
-    v = one(kshape)
+    q = one(qshape, w.descale[0])
+    k = one(kshape, w.descale[1])
+    v = one(kshape, w.descale[2])
     do = one(qshape) if with_do else None
     seqlens = None
     if w.pad_range is not None:
@@ -190,12 +251,13 @@ def draw(w: Workload, seed: int, *, with_do: Optional[bool] = None) -> Inputs:
     if w.butterfly:
         nb = -(-w.seqlen // MASK_BLOCK)
         block_mask = butterfly_block_mask(nb)
-    return Inputs(w, q, k, v, do, seqlens, block_mask, w.scale, w.window)
+    return Inputs(w, q, k, v, do, seqlens, block_mask, w.scale, w.window,
+                  tuple(float(x) for x in w.descale))
 
 
 def draw_case(batch, heads_q, heads_kv, seqlen, head_dim, dtype="bf16", *,
               causal=False, seqlens=None, block_mask=None, seed=0,
-              with_do=True, window=None) -> Inputs:
+              with_do=True, window=None, descale=(1.0, 1.0, 1.0)) -> Inputs:
     """Draw an ad-hoc problem (used by the small parity cases).
 
     ``seqlens`` may be None, a sequence of ints, or "random" (uniform over
@@ -204,7 +266,7 @@ def draw_case(batch, heads_q, heads_kv, seqlen, head_dim, dtype="bf16", *,
     the diagonal always on).
     """
     w = Workload("case", batch, heads_q, heads_kv, seqlen, head_dim, dtype,
-                 causal=causal, backward=with_do)
+                 causal=causal, backward=with_do, descale=tuple(descale))
     inp = draw(w, seed, with_do=with_do)
     rng = np.random.default_rng(seed + 7919)
     if isinstance(seqlens, str) and seqlens == "random":

@@ -61,3 +61,19 @@ def test_draw_case_masks():
     c = draw_case(2, 2, 1, 300, 8, seqlens="random", block_mask="random", seed=5)
     assert c.seqlens.shape == (2,) and c.block_mask.shape == (3, 3)
     assert np.all(np.diag(c.block_mask) == 1)
+
+
+def test_fp8_workloads_encode_scaled_draws():
+    """fp8 inputs are e4m3 codes of x / descale; the logical value
+    descale * decode(code) is within half an e4m3 unit of the fp32 draw."""
+    w = WORKLOADS[10]
+    assert w.dtype == "fp8" and not w.backward and w.descale == (0.0625, 0.0625, 0.0625)
+    assert "fp8" in w.describe() and "descale" in w.describe()
+    small = type(w)("t", 1, 2, 2, 64, 64, "fp8", backward=False, descale=(0.25, 0.5, 2.0))
+    inp = draw(small, 9)
+    assert inp.q.dtype == np.uint8 and inp.descale == (0.25, 0.5, 2.0)
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((1, 2, 64, 64), dtype=np.float32).astype(np.float64)
+    got = inp.as_f64("q")
+    # half a unit: 2^-4 relative (normal range) or 2^-10 * descale absolute
+    assert np.all(np.abs(got - x) <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * 0.25) + 1e-15)
