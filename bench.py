@@ -31,6 +31,7 @@ KERNEL_SOURCES = {
     "decode": ["fa_decode.hip", "fa_stage.h", "fa_device.h"],
     "decode_combine": ["fa_decode.hip"],
     "fwd": ["fa_fwd.hip", "fa_stage.h", "fa_device.h", "fa_philox.h"],
+    "fwd_fp8": ["fa_fwd_fp8.hip", "fa_stage.h", "fa_device.h"],
     "bwd_dkdv": ["fa_bwd.hip", "fa_stage.h", "fa_device.h", "fa_philox.h"],
     "bwd_dq": ["fa_bwd.hip", "fa_stage.h", "fa_device.h", "fa_philox.h"],
     "bwd_pre": ["fa_bwd.hip"],
@@ -272,6 +273,8 @@ def main():
         if w.dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
                 torch.bfloat16).to(dev)
+        if w.dtype == "fp8":
+            return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(dev)
         return torch.from_numpy(a).to(dev)
 
     q, k, v = t(inp.q), t(inp.k), t(inp.v)
@@ -281,7 +284,9 @@ def main():
     kw = dict(scale=inp.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, window=w.window)
     if w.dropout is not None:
         kw.update(dropout_p=w.dropout[0], dropout_seed=w.dropout[1], dropout_offset=w.dropout[2])
-    o = torch.empty_like(q)
+    if w.dtype == "fp8":
+        kw.update(descale=inp.descale)
+    o = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "fp8" else q.dtype, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     if w.backward:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -332,8 +337,9 @@ def main():
     ms_step = wall / args.steps * 1e3
     step_flop = fl["fwd_bwd"] if w.backward else fl["fwd"]
     value = step_flop / (ms_step * 1e-3) / 1e12
-    peak = acc.MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else acc.MFMA_FP32_PEAK_TFLOPS
-    eb = 2 if w.dtype == "bf16" else 4
+    peak = {"bf16": acc.MFMA_BF16_PEAK_TFLOPS, "fp8": acc.MFMA_FP8_PEAK_TFLOPS}.get(
+        w.dtype, acc.MFMA_FP32_PEAK_TFLOPS)
+    eb = {"bf16": 2, "fp8": 1}.get(w.dtype, 4)
 
     kernels = {}
     for name, ms in kern_ms.items():
@@ -351,7 +357,8 @@ def main():
     dk_ = kernels[dom]
     roofline = {"kernel": dom, "bound": dk_["bound"], "achieved": dk_["achieved"],
                 "peak": dk_["peak"], "unit": dk_["unit"], "frac": dk_["frac"],
-                "traffic": recorded_traffic(dom, args.workload)}
+                "traffic": recorded_traffic("fwd_fp8" if w.dtype == "fp8" and dom == "fwd"
+                                            else dom, args.workload)}
 
     fwd_tf = fl["fwd"] / (kern_ms["fwd"] * 1e-3) / 1e12
     rec = {
@@ -366,7 +373,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) inputs, rounded to bf16)",
+        "data": ("synthetic (seeded N(0,1) inputs, encoded as e4m3 of x / descale)"
+                 if w.dtype == "fp8" else "synthetic (seeded N(0,1) inputs, rounded to bf16)"),
         "config": {"workload": w.describe(), "batch": w.batch, "heads_q": w.heads_q,
                    "heads_kv": w.heads_kv, "seqlen": w.seqlen, "head_dim": w.head_dim,
                    "causal": w.causal, "pass": "fwd+bwd" if w.backward else "fwd",

@@ -44,7 +44,7 @@ def fa_strerror(status: int) -> str:
     return _abi.load().fa_strerror(status).decode()
 
 
-_DT = {torch.bfloat16: FA_BF16, torch.float32: FA_FP32}
+_DT = {torch.bfloat16: FA_BF16, torch.float32: FA_FP32, torch.float8_e4m3fn: _abi.FA_FP8_E4M3}
 
 
 def _strides(t: torch.Tensor) -> Strides:
@@ -57,21 +57,23 @@ def _strides(t: torch.Tensor) -> Strides:
 
 def make_params(*, dtype=FA_BF16, o_dtype=None, batch, heads_q, heads_kv, seqlen, head_dim,
                 scale=None, causal=False, seqlens_k=0, block_mask=0, block_mask_ld=0,
-                window=None, dropout_p=0.0, dropout_seed=0, dropout_offset=0) -> Params:
+                window=None, dropout_p=0.0, dropout_seed=0, dropout_offset=0,
+                descale=(1.0, 1.0, 1.0)) -> Params:
     """fa_params from plain values (device pointers as ints); ``window`` is
     None or a (left, right) sliding-window band; ``dropout_p`` (stored as
     float32), ``dropout_seed`` (uint64) and ``dropout_offset`` (uint32) select
-    the in-kernel dropout."""
+    the in-kernel dropout; ``descale`` the (q, k, v) factors of FP8 inputs."""
     wl, wr = (0, 0) if window is None else (int(window[0]), int(window[1]))
     return Params(dtype, dtype if o_dtype is None else o_dtype, batch, heads_q, heads_kv, seqlen,
                   head_dim, 1.0 / math.sqrt(head_dim) if scale is None else scale, int(bool(causal)),
                   seqlens_k or None, block_mask or None, block_mask_ld,
                   int(window is not None), wl, wr, float(dropout_p), int(dropout_offset),
-                  int(dropout_seed))
+                  int(dropout_seed), float(descale[0]), float(descale[1]), float(descale[2]))
 
 
 def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype, window,
-                 dropout_p=0.0, dropout_seed=0, dropout_offset=0) -> Params:
+                 dropout_p=0.0, dropout_seed=0, dropout_offset=0,
+                 descale=(1.0, 1.0, 1.0)) -> Params:
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if k.dtype != q.dtype:
@@ -96,7 +98,7 @@ def _params_from(q, k, *, scale, causal, seqlens_k, block_mask, o_dtype, window,
                        seqlen=N, head_dim=d, scale=scale, causal=causal, seqlens_k=sl_ptr,
                        block_mask=bm_ptr, block_mask_ld=bm_ld, window=window,
                        dropout_p=dropout_p, dropout_seed=dropout_seed,
-                       dropout_offset=dropout_offset)
+                       dropout_offset=dropout_offset, descale=descale)
 
 
 def _stream() -> ctypes.c_void_p:
@@ -120,13 +122,20 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
            block_mask: Optional[torch.Tensor] = None, o_dtype: Optional[torch.dtype] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            tile_log: bool = False, window: Optional[tuple] = None, dropout_p: float = 0.0,
-           dropout_seed: int = 0, dropout_offset: int = 0):
-    """Forward pass. Returns (O, LSE, tile_log or None)."""
+           dropout_seed: int = 0, dropout_offset: int = 0, descale=(1.0, 1.0, 1.0)):
+    """Forward pass. Returns (O, LSE, tile_log or None).
+
+    float8_e4m3fn q, k, v select the FP8 forward: ``descale`` gives the
+    per-tensor (q, k, v) factors, and O defaults to bfloat16.
+    """
     lib = _abi.load()
+    fp8 = q.dtype == torch.float8_e4m3fn
+    if fp8 and o_dtype is None:
+        o_dtype = torch.bfloat16
     p = _params_from(q, k, scale=scale, causal=causal, seqlens_k=seqlens_k,
                      block_mask=block_mask, o_dtype=o_dtype, window=window,
                      dropout_p=dropout_p, dropout_seed=dropout_seed,
-                     dropout_offset=dropout_offset)
+                     dropout_offset=dropout_offset, descale=descale)
     B, Hq, N, d = q.shape
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=o_dtype or q.dtype, device=q.device)

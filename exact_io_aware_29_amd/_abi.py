@@ -25,6 +25,7 @@ STATUS_CODES = [FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE, FA_ERR_HEADDIM, 
 
 FA_BF16 = 0
 FA_FP32 = 1
+FA_FP8_E4M3 = 2
 FA_MASK_BLOCK = 128
 
 
@@ -52,6 +53,9 @@ class Params(ctypes.Structure):
         ("dropout_p", ctypes.c_float),
         ("dropout_offset", ctypes.c_uint32),
         ("dropout_seed", ctypes.c_uint64),
+        ("descale_q", ctypes.c_float),
+        ("descale_k", ctypes.c_float),
+        ("descale_v", ctypes.c_float),
     ]
 
 

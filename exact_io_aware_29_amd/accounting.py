@@ -33,6 +33,7 @@ import numpy as np
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 / fp16 matrix peak
 MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X published fp32 matrix/vector peak
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X published dense fp8 matrix peak
 HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
 
 

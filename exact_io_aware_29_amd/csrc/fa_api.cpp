@@ -27,7 +27,7 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
-size_t elem_size(int dtype) { return dtype == FA_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype == FA_BF16 ? 2 : dtype == FA_FP8_E4M3 ? 1 : 4; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -38,8 +38,8 @@ int64_t keep_threshold(float p) {
 
 int check_params(const fa_params* p) {
   if (!p) return fail(FA_ERR_NULL, "params is NULL");
-  if (p->dtype != FA_BF16 && p->dtype != FA_FP32)
-    return fail(FA_ERR_DTYPE, "dtype %d is not FA_BF16 or FA_FP32", p->dtype);
+  if (p->dtype != FA_BF16 && p->dtype != FA_FP32 && p->dtype != FA_FP8_E4M3)
+    return fail(FA_ERR_DTYPE, "dtype %d is not FA_BF16, FA_FP32 or FA_FP8_E4M3", p->dtype);
   if (p->o_dtype != FA_BF16 && p->o_dtype != FA_FP32)
     return fail(FA_ERR_DTYPE, "o_dtype %d is not FA_BF16 or FA_FP32", p->o_dtype);
   if (p->dtype == FA_FP32 && p->o_dtype != FA_FP32)
@@ -64,6 +64,13 @@ int check_params(const fa_params* p) {
     return fail(FA_ERR_DROPOUT, "dropout_p must lie in [0, 1) (got %g)", (double)p->dropout_p);
   if (p->dropout_p > 0.f && keep_threshold(p->dropout_p) <= 0)
     return fail(FA_ERR_DROPOUT, "dropout_p %g drops every element", (double)p->dropout_p);
+  if (p->dtype == FA_FP8_E4M3) {
+    const float ds[3] = {p->descale_q, p->descale_k, p->descale_v};
+    for (float x : ds)
+      if (!std::isfinite(x) || !(x > 0.f))
+        return fail(FA_ERR_SCALE, "FP8 descale factors must be finite and positive");
+    if (p->dropout_p != 0.f) return fail(FA_ERR_DROPOUT, "the FP8 forward takes no dropout");
+  }
   if (p->block_mask && p->block_mask_ld < blocks)
     return fail(FA_ERR_MASK, "block_mask_ld %d < ceil(seqlen/128) = %lld", p->block_mask_ld,
                 (long long)blocks);
@@ -165,8 +172,12 @@ int fa_fwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   a.lse = lse;
   a.log = tile_log;
   a.o_fp32 = p->o_dtype == FA_FP32;
-  const hipError_t e =
-      fa::launch_fwd(a, p->dtype == FA_BF16 ? 0 : 1, p->head_dim, static_cast<hipStream_t>(stream));
+  a.qk_descale = p->descale_q * p->descale_k;
+  a.v_descale = p->descale_v;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = p->dtype == FA_FP8_E4M3
+                           ? fa::launch_fwd_fp8(a, p->head_dim, st)
+                           : fa::launch_fwd(a, p->dtype == FA_BF16 ? 0 : 1, p->head_dim, st);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return FA_OK;
 }

@@ -42,6 +42,8 @@ struct FwdArgs {
   float* lse;
   uint32_t* log;
   int o_fp32;
+  float qk_descale;  // FP8 inputs: descale_q * descale_k (scores) ...
+  float v_descale;   // ... and descale_v (output)
 };
 
 struct BwdArgs {
@@ -81,6 +83,7 @@ struct DecodeArgs {
 
 // Launchers (defined next to their kernels). dtype: 0 bf16, 1 fp32.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_fwd_fp8(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);

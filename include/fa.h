@@ -79,7 +79,13 @@ enum fa_status {
 /* Element types. */
 enum fa_dtype {
   FA_BF16 = 0, /* bfloat16 storage; all arithmetic accumulates in fp32 */
-  FA_FP32 = 1  /* float32 storage and fp32 matrix-core arithmetic */
+  FA_FP32 = 1, /* float32 storage and fp32 matrix-core arithmetic */
+  /* OCP e4m3 (E4M3FN) codes of Q, K, V, forward only: the logical inputs
+   * are descale_x * decode(code); S on the FP8 matrix core (fp32
+   * accumulation), softmax in fp32, P~ rounded to e4m3 for the PV product.
+   * Not exact attention: FlashAttention-3's FP8 direction (cross-paper
+   * synthesis page, section 2). O must be FA_BF16 or FA_FP32. */
+  FA_FP8_E4M3 = 2
 };
 
 /* Granularity of block masks and of tile logs (rows and columns). */
@@ -134,6 +140,12 @@ typedef struct fa_params {
   float dropout_p;
   uint32_t dropout_offset;
   uint64_t dropout_seed;
+  /* FA_FP8_E4M3 inputs only: per-tensor factors that turn codes into values
+   * (each finite and > 0, FA_ERR_SCALE otherwise); ignored for other
+   * dtypes. The FP8 forward takes no dropout (FA_ERR_DROPOUT). */
+  float descale_q;
+  float descale_k;
+  float descale_v;
 } fa_params;
 
 /*

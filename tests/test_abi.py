@@ -52,7 +52,7 @@ def test_status_codes_match_header():
     for name in ("FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_DTYPE", "FA_ERR_HEADDIM",
                  "FA_ERR_GQA", "FA_ERR_STRIDE", "FA_ERR_ALIGN", "FA_ERR_WORKSPACE",
                  "FA_ERR_HIP", "FA_ERR_MASK", "FA_ERR_SCALE", "FA_ERR_DROPOUT", "FA_BF16",
-                 "FA_FP32"):
+                 "FA_FP32", "FA_FP8_E4M3"):
         assert codes[name] == getattr(_abi, name), name
     msgs = {fa.fa_strerror(c) for c in _abi.STATUS_CODES}
     assert len(msgs) == len(_abi.STATUS_CODES)
@@ -104,6 +104,12 @@ def _fwd(p, q=P16, k=P32, v=P48, o=P64, lse=P80, sq=None, sk=None, so=None, log=
     (dict(dropout_p=-0.1), _abi.FA_ERR_DROPOUT),
     (dict(dropout_p=math.nan), _abi.FA_ERR_DROPOUT),
     (dict(dropout_p=0.999995), _abi.FA_ERR_DROPOUT),  # T = round(0.33) = 0
+    (dict(dtype=_abi.FA_FP8_E4M3, o_dtype=_abi.FA_BF16, descale=(1.0, 0.0, 1.0)),
+     _abi.FA_ERR_SCALE),
+    (dict(dtype=_abi.FA_FP8_E4M3, o_dtype=_abi.FA_BF16, descale=(1.0, 1.0, math.inf)),
+     _abi.FA_ERR_SCALE),
+    (dict(dtype=_abi.FA_FP8_E4M3, o_dtype=_abi.FA_FP8_E4M3), _abi.FA_ERR_DTYPE),
+    (dict(dtype=_abi.FA_FP8_E4M3, o_dtype=_abi.FA_BF16, dropout_p=0.1), _abi.FA_ERR_DROPOUT),
     (dict(batch=1 << 20, heads_q=1 << 10, heads_kv=1 << 10, seqlen=1 << 20), _abi.FA_ERR_SHAPE),
 ])
 def test_fwd_rejects_bad_params(mut, code):
@@ -219,3 +225,18 @@ def test_decode_rejects_dropout_window_and_mask():
     assert call(dropout_p=0.1) == _abi.FA_ERR_DROPOUT
     assert call(window=(4, 0)) == _abi.FA_ERR_MASK
     assert call(dtype=_abi.FA_FP32, o_dtype=_abi.FA_FP32) == _abi.FA_ERR_DTYPE
+
+
+@no_gpu_only
+def test_fp8_is_forward_only():
+    """The backward and decode reject FP8 inputs; FP8 strides are in bytes
+    (multiples of 16)."""
+    lib = fa.library()
+    p = _params(dtype=_abi.FA_FP8_E4M3, o_dtype=_abi.FA_BF16)
+    s8 = _abi.Strides(4 * 300 * 64, 300 * 64, 64)
+    assert _fwd(p, sq=_abi.Strides(4 * 300 * 72, 300 * 72, 72))[0] == _abi.FA_ERR_STRIDE
+    s, skv = _strides(p), _strides(p, p.heads_kv)
+    st = lib.fa_bwd(ctypes.byref(p), P16, s8, P32, s8, P48, s8, P64, s, P80, s8,
+                    ctypes.c_void_p(0x6000), P16, s8, P32, s8, P48, s8, ctypes.c_void_p(0x7000),
+                    1 << 30, None, None, None)
+    assert st == _abi.FA_ERR_DTYPE
