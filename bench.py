@@ -34,7 +34,6 @@ KERNEL_SOURCES = {
     "fwd_fp8": ["fa_fwd_fp8.hip", "fa_stage.h", "fa_device.h"],
     "bwd_dkdv": ["fa_bwd.hip", "fa_stage.h", "fa_device.h", "fa_philox.h"],
     "bwd_dq": ["fa_bwd.hip", "fa_stage.h", "fa_device.h", "fa_philox.h"],
-    "bwd_pre": ["fa_bwd.hip"],
 }
 
 
@@ -302,13 +301,13 @@ def main():
             ev[1].record()
         if w.backward:
             fa.fa_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws,
-                      stage_events=None if ev is None else ev[2:6], **kw)
+                      stage_events=None if ev is None else ev[2:5], **kw)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for ev in events:
         for e in ev:
             e.record()  # create the events outside the timed region
@@ -327,7 +326,7 @@ def main():
 
     kern_ms = {"fwd": avg_ms(0, 1)}
     if w.backward:
-        kern_ms.update(bwd_pre=avg_ms(2, 3), bwd_dkdv=avg_ms(3, 4), bwd_dq=avg_ms(4, 5))
+        kern_ms.update(bwd_dq=avg_ms(2, 3), bwd_dkdv=avg_ms(3, 4))
 
     per_b = [int(acc.allowed_pairs_per_row(
         w.seqlen, causal=w.causal, seqlen_k=None if inp.seqlens is None else int(inp.seqlens[b]),
@@ -339,20 +338,12 @@ def main():
     value = step_flop / (ms_step * 1e-3) / 1e12
     peak = {"bf16": acc.MFMA_BF16_PEAK_TFLOPS, "fp8": acc.MFMA_FP8_PEAK_TFLOPS}.get(
         w.dtype, acc.MFMA_FP32_PEAK_TFLOPS)
-    eb = {"bf16": 2, "fp8": 1}.get(w.dtype, 4)
 
     kernels = {}
     for name, ms in kern_ms.items():
-        if name == "bwd_pre":
-            nbytes = acc.bwd_pre_bytes(w.batch, w.heads_q, w.seqlen, w.head_dim, eb, eb)
-            ach = nbytes / (ms * 1e-3) / 1e9
-            kernels[name] = {"ms": round(ms, 4), "bound": "hbm", "achieved": round(ach, 1),
-                             "peak": acc.HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(ach / acc.HBM_PEAK_GBS, 4)}
-        else:
-            ach = fl[name] / (ms * 1e-3) / 1e12
-            kernels[name] = {"ms": round(ms, 4), "bound": "mfma", "achieved": round(ach, 1),
-                             "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+        ach = fl[name] / (ms * 1e-3) / 1e12
+        kernels[name] = {"ms": round(ms, 4), "bound": "mfma", "achieved": round(ach, 1),
+                         "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     dom = max(kern_ms, key=kern_ms.get)
     dk_ = kernels[dom]
     roofline = {"kernel": dom, "bound": dk_["bound"], "achieved": dk_["achieved"],

@@ -164,8 +164,9 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
            dropout_offset: int = 0):
     """Backward pass. Returns (dQ, dK, dV, tile_log or None).
 
-    ``stage_events``: optional 4 ``torch.cuda.Event`` objects, recorded by
-    the library around its three kernels (for per-kernel timing). The
+    ``stage_events``: optional 3 ``torch.cuda.Event`` objects, recorded by
+    the library before its dQ kernel, between it and the dK/dV kernel, and
+    after that (for per-kernel timing). The
     dropout arguments must be those of the forward that produced ``o``.
     """
     lib = _abi.load()
@@ -190,7 +191,9 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
             if ev.cuda_event == 0:
                 ev.record()  # materialise the underlying hipEvent_t
             handles.append(ev.cuda_event)
-        ev_arr = (ctypes.c_void_p * 4)(*handles)
+        if len(handles) != 3:
+            raise ValueError("stage_events takes 3 events")
+        ev_arr = (ctypes.c_void_p * 3)(*handles)
     st = lib.fa_bwd(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                     _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
                     _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),

@@ -154,11 +154,6 @@ def bytes_models(B, Hq, Hkv, N, d, eb, *, tiles, o_eb=None) -> dict:
     }
 
 
-def bwd_pre_bytes(B, Hq, N, d, eb, o_eb) -> int:
-    """Algorithmic bytes of the D = rowsum(dO * O) kernel: read dO and O, write D."""
-    return B * Hq * N * (d * (eb + o_eb) + 4)
-
-
 def score_matrix_bytes(heads: int, seqlen: int, eb: int) -> int:
     """Bytes of the full heads x N x N score matrix at eb bytes per element."""
     return heads * seqlen * seqlen * eb

@@ -209,7 +209,7 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   if (tile_log && reinterpret_cast<uintptr_t>(tile_log) % 4)
     return fail(FA_ERR_ALIGN, "tile_log is not 4-byte aligned");
   if (stage_events)
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
       if (!stage_events[i]) return fail(FA_ERR_NULL, "stage_events[%d] is NULL", i);
 
   fa::BwdArgs a;
@@ -243,13 +243,12 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
     return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) : hipSuccess;
   };
   hipError_t e;
+  // dQ first: it also writes the row statistics the dK/dV kernel reads.
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = fa::launch_bwd_pre(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_pre launch");
+  if ((e = fa::launch_bwd_dq(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_dq launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = fa::launch_bwd_dkdv(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_dkdv launch");
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = fa::launch_bwd_dq(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_dq launch");
-  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event record");
   return FA_OK;
 }
 

@@ -3,81 +3,36 @@
 // The forward kept only O and LSE = m + ln l per row (FlashAttention
 // deep-reading report, zako-mio, sections 2.5 and 3.3: no N x N matrix is
 // stored; S and P are rebuilt on chip from Q, K and the row statistic).
-// Three kernels, in stream order:
+// Two kernels, in stream order:
 //
-//   bwd_pre   D_i = dO_i . O_i                       (memory-bound row dots)
+//   bwd_dq    one workgroup per 128 query rows, 32 rows per wave; first the
+//             row statistics D_i = dO_i . O_i and LSE_i log2e of its rows
+//             (stored for the next kernel), then for every visited K/V
+//             tile: S^T = K Q^T, dP^T = V dO^T, dS^T = P (dP - D),
+//             dQ^T += K^T dS^T                      (fp32 in registers)
 //   bwd_dkdv  one workgroup per 128 keys of one K/V head, 32 keys per wave;
 //             for every query head of the group and every visited block of
 //             query rows:  S = Q K^T,  P = 2^(S scale log2e - LSE log2e),
 //             dP = dO V^T,  dS = P (dP - D),
 //             dV^T += dO^T P,  dK^T += Q^T dS        (fp32 in registers)
-//   bwd_dq    one workgroup per 128 query rows, 32 rows per wave; for every
-//             visited K/V tile: S^T = K Q^T, dP^T = V dO^T, dS^T as above,
-//             dQ^T += K^T dS^T
 //
 // D_i = sum_j P_ij dP_ij equals dO_i . O_i because O_i = sum_j P_ij V_j;
-// computing it from the stored O costs one pass over O and dO instead of a
-// second reduction per tile. All gradients stay in fp32 registers for the
+// computing it from the stored O costs one read of O instead of a second
+// reduction per tile, and the dQ kernel, which already holds the row's dO,
+// does it in its prologue. All gradients stay in fp32 registers for the
 // whole key (or query) block and are written once; there are no atomics.
 #include "fa_philox.h"
 #include "fa_stage.h"
 
 namespace fa {
 
-__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-
-// ----------------------------------------------------------------- D = rowsum(dO * O)
+// ----------------------------------------------------------------- row statistics
 
 // LSE in base-2 units; an empty row (LSE = -inf) becomes +inf so that every
 // rebuilt probability of that row is 2^-inf = 0.
 __device__ __forceinline__ float lse2_of(float lse) {
   return lse == -kInf ? kInf : lse * kLog2e;
 }
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int TPR = D / 8;  // lanes per row, 8 elements each
-  constexpr int RPB = 256 / TPR;
-  const Problem& p = a.p;
-  const int64_t rows = (int64_t)p.B * p.Hq * p.N;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int part = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const int64_t i = row % p.N;
-    const int64_t bh = row / p.N;
-    const int64_t h = bh % p.Hq, b = bh / p.Hq;
-    Chunk g;
-    g.v = *reinterpret_cast<const uint4*>(static_cast<const bf16*>(a.dout) + b * a.sdo.b +
-                                          h * a.sdo.h + i * a.sdo.n + part * 8);
-    if (a.o_fp32) {
-      const float* op = static_cast<const float*>(a.o) + b * a.so.b + h * a.so.h + i * a.so.n + part * 8;
-      const float4 o0 = *reinterpret_cast<const float4*>(op);
-      const float4 o1 = *reinterpret_cast<const float4*>(op + 4);
-      acc = bf16_lo(g.d[0]) * o0.x + bf16_hi(g.d[0]) * o0.y + bf16_lo(g.d[1]) * o0.z +
-            bf16_hi(g.d[1]) * o0.w + bf16_lo(g.d[2]) * o1.x + bf16_hi(g.d[2]) * o1.y +
-            bf16_lo(g.d[3]) * o1.z + bf16_hi(g.d[3]) * o1.w;
-    } else {
-      Chunk o;
-      o.v = *reinterpret_cast<const uint4*>(static_cast<const bf16*>(a.o) + b * a.so.b +
-                                            h * a.so.h + i * a.so.n + part * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc += bf16_lo(g.d[e]) * bf16_lo(o.d[e]) + bf16_hi(g.d[e]) * bf16_hi(o.d[e]);
-    }
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (part == 0 && row < rows) {
-    // Under dropout the kernels use q D (q the keep probability): with
-    // dP = (Z / q) o dO V^T, dS = P o (dP - D) = (1 / q) P o (Z o dO V^T - q D),
-    // and the 1 / q joins the final scale of dQ and dK.
-    a.dvec[row] = a.p.drop ? acc * a.p.drop_q : acc;
-    a.lse2[row] = lse2_of(a.lse[row]);
-  }
-}
-
 
 // ----------------------------------------------------------------- dK, dV
 
@@ -474,9 +429,42 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       dof[kk] = frag_g(dOp + 16 * kk, qok);
     }
   }
+  // Row statistics of this lane's row, computed here and stored for the
+  // dK/dV kernel, which runs after this one: D = dO . O (the two lane halves
+  // hold interleaved halves of the row), q D under dropout (with
+  // dP = (Z / q) o dO V^T, dS = P o (dP - D) = (1 / q) P o (Z o dO V^T - q D),
+  // and the 1 / q joins the final scales), and the LSE in base-2 units
+  // (+inf for a row with no allowed key, so that every rebuilt probability
+  // of it is 2^-inf = 0).
   const int64_t rowstat = ((int64_t)b * p.Hq + h) * p.N + (qok ? my_q : 0);
-  const float lse2 = qok ? a.lse2[rowstat] : kInf;
-  const float dq_d = qok ? a.dvec[rowstat] : 0.f;
+  float dpart = 0.f;
+  if (qok) {
+    const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      float o8[8];
+      if (a.o_fp32) {
+        const float* op = static_cast<const float*>(a.o) + orow + 16 * kk;
+        const float4 x0 = *reinterpret_cast<const float4*>(op);
+        const float4 x1 = *reinterpret_cast<const float4*>(op + 4);
+        o8[0] = x0.x; o8[1] = x0.y; o8[2] = x0.z; o8[3] = x0.w;
+        o8[4] = x1.x; o8[5] = x1.y; o8[6] = x1.z; o8[7] = x1.w;
+      } else {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.o) + orow + 16 * kk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = (float)x[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[kk][e], o8[e], dpart);
+    }
+  }
+  const float dsum = half_sum(dpart);
+  const float dq_d = p.drop ? dsum * p.drop_q : dsum;
+  const float lse2 = qok ? lse2_of(a.lse[rowstat]) : kInf;
+  if (qok && hh == 0) {
+    a.dvec[rowstat] = dq_d;
+    a.lse2[rowstat] = lse2;
+  }
 
   int kvo[T::NLD], vvo[T::NLD];
   dma_offsets<D, C::BC>(kvo, ksb, w, lane);
@@ -597,17 +585,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------- launchers
-
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t s) {
-  const int64_t rows = (int64_t)a.p.B * a.p.Hq * a.p.N;
-  const int rpb = 256 / (head_dim / 8);
-  const int64_t grid = (rows + rpb - 1) / rpb;
-  if (head_dim == 64)
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t grid = (int64_t)((a.p.N + 127) / 128) * a.p.Hkv * a.p.B;

@@ -55,8 +55,9 @@ struct BwdArgs {
   const void* dout;
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   const float* lse;
-  float* dvec;  // workspace: D = rowsum(dO * O), fp32 [B][Hq][N]
-  float* lse2;  // workspace: LSE * log2(e) (+inf for empty rows), fp32 [B][Hq][N]
+  float* dvec;  // workspace: D = rowsum(dO * O) (q D under dropout), fp32 [B][Hq][N],
+                // written by the dQ kernel and read by the dK/dV kernel
+  float* lse2;  // workspace: LSE * log2(e) (+inf for empty rows), fp32 [B][Hq][N], likewise
   void* dq;
   void* dk;
   void* dv;
@@ -84,7 +85,6 @@ struct DecodeArgs {
 // Launchers (defined next to their kernels). dtype: 0 bf16, 1 fp32.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int head_dim, hipStream_t s);
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s);

@@ -178,20 +178,21 @@ int fa_fwd(const fa_params* p,
 size_t fa_tile_log_words(const fa_params* p);
 
 /* Bytes of device workspace fa_bwd needs: two fp32 [B][Hq][N] row vectors,
- * D and the log-sum-exp in base-2 units. */
+ * D (q D under dropout) and the log-sum-exp in base-2 units, written by the
+ * dQ kernel and read by the dK/dV kernel. */
 size_t fa_bwd_workspace_size(const fa_params* p);
 
 /*
  * fa_bwd -- recomputation backward (the report's sections 2.5 and 3.3; the
- * tutorial's backward paragraph). Three kernels run in order on `stream`:
- *   1. D_i = sum_t dO[i][t] * O[i][t] and LSE_i * log2(e) into the
- *      workspace (fp32; +inf for a row with no allowed key);
- *   2. per block of 128 keys of one key/value head: for every query head of
- *      its group and every visited query tile, rebuild
+ * tutorial's backward paragraph). Two kernels run in order on `stream`:
+ *   1. per block of 128 query rows: D_i = sum_t dO[i][t] * O[i][t] and
+ *      LSE_i * log2(e) of its rows into the workspace (fp32; +inf for a row
+ *      with no allowed key); then for every visited key tile rebuild
  *      P = exp(scale * q.k - LSE), dP = dO V^T, dS = P * (dP - D) and
- *      accumulate dV += P^T dO and dK += scale * dS^T Q (fp32 registers);
- *   3. per block of 128 query rows: rebuild P and dS the same way and
- *      accumulate dQ += scale * dS K.
+ *      accumulate dQ += scale * dS K (fp32 registers);
+ *   2. per block of 128 keys of one key/value head: for every query head of
+ *      its group and every visited query tile, rebuild P and dS the same
+ *      way and accumulate dV += P^T dO and dK += scale * dS^T Q.
  *
  *   q, k, v, o, dout  device inputs (o of dtype p->o_dtype, the others of
  *                     p->dtype) with their strides
@@ -200,11 +201,11 @@ size_t fa_bwd_workspace_size(const fa_params* p);
  *   workspace         device buffer of >= fa_bwd_workspace_size(p) bytes,
  *                     16-byte aligned; its contents on entry are ignored
  *   tile_log          NULL, or caller-zeroed 2 * fa_tile_log_words(p) words:
- *                     first the tiles visited by kernel 2, then by kernel 3
- *                     (same bit layout as fa_fwd)
- *   stage_events      NULL, or 4 hipEvent_t recorded on `stream` before
- *                     kernel 1, before kernel 2, before kernel 3 and after
- *                     kernel 3 (for per-kernel timing)
+ *                     first the tiles visited by kernel 2 (dK/dV), then by
+ *                     kernel 1 (dQ) (same bit layout as fa_fwd)
+ *   stage_events      NULL, or 3 hipEvent_t recorded on `stream` before
+ *                     kernel 1, between the kernels and after kernel 2 (for
+ *                     per-kernel timing)
  * Supports dtype FA_BF16 only (FA_ERR_DTYPE otherwise).
  */
 int fa_bwd(const fa_params* p,

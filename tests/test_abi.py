@@ -153,7 +153,7 @@ def test_bwd_validation():
     assert call(ws=ctypes.c_void_p(0x7008)) == _abi.FA_ERR_ALIGN
     p32 = _params(dtype=_abi.FA_FP32, o_dtype=_abi.FA_FP32)
     assert call(p=p32) == _abi.FA_ERR_DTYPE
-    ev = (ctypes.c_void_p * 4)(1, 2, None, 4)
+    ev = (ctypes.c_void_p * 3)(1, None, 3)
     assert call(ev=ctypes.cast(ev, ctypes.c_void_p)) == _abi.FA_ERR_NULL
     assert "stage_events" in lib.fa_last_error_detail().decode()
 
