@@ -512,6 +512,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       f32x16 st = f32x16{}, dpt = f32x16{};
       const char* kp = Ks + 32 * t * T::RB;
       const char* vp = Vs + 32 * t * T::RB;
+      // Raised priority while this wave feeds the matrix pipe, so that the
+      // other wave on the SIMD fills the VALU between its products.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int k4 = 0; k4 < C::NKK; k4 += 4) {
         bf16x8 ka[4], va[4];
@@ -526,6 +529,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           dpt = mfma(va[i], dof[k4 + i], dpt);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
       if (__builtin_expect(need_mask, false)) {  // boundary tiles only
@@ -552,6 +556,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (dpt[r] - dq_d);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 dsf = pack8(dpt, c);
@@ -560,6 +565,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         for (int db = 0; db < C::NDB; ++db)
           acc[db] = mfma(lds_tr(ktp, troff[db][0], troff[db][1]), dsf, acc[db]);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (nxt < ntiles) {
       wait_dma();

@@ -224,15 +224,29 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   const float* ls = a.ws_lse + row * a.splits;
   float m = -kInf;
   for (int s = 0; s < a.splits; ++s) m = fmaxf(m, ls[s]);
+  const float mref = m == -kInf ? 0.f : m;  // every split empty: all weights 0
   float wsum = 0.f;
   float o[D / 64] = {};
-  for (int s = 0; s < a.splits; ++s) {
-    if (ls[s] == -kInf) continue;
-    const float f = __builtin_amdgcn_exp2f(ls[s] - m);
-    wsum += f;
-    const float* os = a.ws_o + (row * a.splits + s) * D;
+  // Splits in batches of 8 whose loads are independent, so their latencies
+  // overlap instead of adding up one split after another.
+  for (int s0 = 0; s0 < a.splits; s0 += 8) {
+    float f[8], x[8][D / 64];
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j) o[j] += f * os[threadIdx.x + 64 * j];
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u;
+      const float l = s < a.splits ? ls[s] : -kInf;
+      const bool ok = l != -kInf;  // an empty split's partial is never read
+      f[u] = ok ? __builtin_amdgcn_exp2f(l - mref) : 0.f;
+      const float* os = a.ws_o + (row * a.splits + (ok ? s : 0)) * D;
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) x[u][j] = ok ? os[threadIdx.x + 64 * j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      wsum += f[u];
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) o[j] = fmaf(f[u], x[u][j], o[j]);
+    }
   }
   char* obase = static_cast<char*>(a.o);
 #pragma unroll
