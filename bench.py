@@ -93,6 +93,35 @@ def cpu_baseline(inp, pairs_per_head, budget_s):
                                                        w.dropout[1], w.dropout[2])
     done, flop = 0, 0
     t0 = time.perf_counter()
+    if w.seqlen > 8192:
+        # One whole head would take minutes: time row chunks of head (0, 0)
+        # instead -- the forward and the dQ part of the backward (S, dP, dQ
+        # rebuilt for those rows), counted as (4 + 6) d per allowed pair.
+        from exact_io_aware_29_amd import accounting as acc
+        m = mask_for(0, causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask,
+                     window=w.window)
+        per_row = acc.allowed_pairs_per_row(
+            w.seqlen, causal=w.causal, seqlen_k=None if inp.seqlens is None else int(inp.seqlens[0]),
+            block_mask=inp.block_mask, window=w.window)
+        q, k, v = inp.as_f64("q", (0, 0)), inp.as_f64("k", (0, 0)), inp.as_f64("v", (0, 0))
+        do = inp.as_f64("do", (0, 0)) if w.backward else None
+        drop = None if dr is None else dr.head(0)
+        rows_done = 0
+        for r0 in range(0, w.seqlen, 256):
+            rows = np.arange(r0, min(r0 + 256, w.seqlen))
+            oracle.head_forward(q, k, v, inp.scale, m, rows=rows, drop=drop)
+            if w.backward:
+                oracle.head_backward(q, k, v, do, inp.scale, m, q_rows=rows, drop=drop)
+            rows_done += len(rows)
+            flop += ((4 + 6) if w.backward else 4) * w.head_dim * int(per_row[rows].sum())
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+        return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+                "kind": "oracle", "cpu": cpu_model(),
+                "sample": f"fp64 oracle forward{' and the dQ part of the backward' if w.backward else ''}"
+                          f" over the first {rows_done} rows of (batch 0, head 0), {el:.1f} s; "
+                          f"{'(4 + 6)' if w.backward else '4'} d flops per allowed pair"}
     for b in range(w.batch):
         m = mask_for(b, causal=w.causal, seqlens=inp.seqlens, block_mask=inp.block_mask,
                      window=w.window)
@@ -116,6 +145,7 @@ def cpu_baseline(inp, pairs_per_head, budget_s):
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": f"fp64 oracle {'fwd+bwd' if w.backward else 'fwd'} of the first {done} (batch, head) pairs of "
                   f"{w.batch * w.heads_q}, {el:.1f} s; same algorithmic flop count",
     }
@@ -145,7 +175,7 @@ def decode_cpu_baseline(inp, budget_s):
             break
     el = time.perf_counter() - t0
     return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"fp64 oracle decode of the first {done} of {w.batch} sequences, "
                       f"{el:.1f} s; same algorithmic bytes"}
 
@@ -214,6 +244,7 @@ def decode_main(args, w, inp, dev):
                    "heads_kv": w.heads_kv, "cache_len": w.seqlen, "head_dim": w.head_dim,
                    "pass": "decode"},
         "algorithmic_bytes": nbytes,
+        "device": device_info(),
         "kernels": kernels,
         "roofline": dict(kernel="decode", **{k_: kernels["decode"][k_] for k_ in
                                              ("bound", "achieved", "peak", "unit", "frac")},
@@ -230,6 +261,24 @@ def decode_traffic(workload: int):
     a = recorded_traffic("decode", workload)
     b = recorded_traffic("decode_combine", workload)
     return None if a is None or b is None else a + b
+
+
+def device_info():
+    """Name, compute units and architecture of the GPU the numbers come from."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "compute_units": pr.multi_processor_count,
+            "arch": getattr(pr, "gcnArchName", "")}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_calibration(args, dev):
@@ -321,12 +370,14 @@ def main():
 
     copy_calibration(args, dev)
 
-    def avg_ms(a, b):
-        return float(np.mean([events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)]))
+    def times(a, b):
+        return np.array([events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)])
 
-    kern_ms = {"fwd": avg_ms(0, 1)}
+    spans = {"fwd": (0, 1)}
     if w.backward:
-        kern_ms.update(bwd_dq=avg_ms(2, 3), bwd_dkdv=avg_ms(3, 4))
+        spans.update(bwd_dq=(2, 3), bwd_dkdv=(3, 4))
+    kern_t = {k: times(*v) for k, v in spans.items()}
+    kern_ms = {k: float(t.mean()) for k, t in kern_t.items()}
 
     per_b = [int(acc.allowed_pairs_per_row(
         w.seqlen, causal=w.causal, seqlen_k=None if inp.seqlens is None else int(inp.seqlens[b]),
@@ -342,8 +393,15 @@ def main():
     kernels = {}
     for name, ms in kern_ms.items():
         ach = fl[name] / (ms * 1e-3) / 1e12
-        kernels[name] = {"ms": round(ms, 4), "bound": "mfma", "achieved": round(ach, 1),
+        kernels[name] = {"ms": round(ms, 4), "ms_median": round(float(np.median(kern_t[name])), 4),
+                         "ms_min": round(float(kern_t[name].min()), 4),
+                         "bound": "mfma", "achieved": round(ach, 1),
                          "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+    # Work the tile structure executes: every visited 128 x 128 tile counted
+    # in full (the algorithmic count above takes only the allowed pairs).
+    tiles = acc.visited_tiles(w.batch, w.heads_q, w.seqlen, causal=w.causal,
+                              seqlens=inp.seqlens, block_mask=inp.block_mask, window=w.window)
+    tile_fl = acc.flops(tiles * 128 * 128, w.head_dim)
     dom = max(kern_ms, key=kern_ms.get)
     dk_ = kernels[dom]
     roofline = {"kernel": dom, "bound": dk_["bound"], "achieved": dk_["achieved"],
@@ -374,6 +432,8 @@ def main():
         "fwd_tflops": round(fwd_tf, 2),
         "pct_of_peak_fwd": round(100 * fwd_tf / peak, 2),
         "algorithmic_flop": {"fwd": fl["fwd"], "fwd_bwd": fl["fwd_bwd"], "pairs": pairs},
+        "tile_flop": {"fwd": tile_fl["fwd"], "fwd_bwd": tile_fl["fwd_bwd"], "tiles_128": tiles},
+        "device": device_info(),
         "kernels": kernels,
         "roofline": roofline,
     }
