@@ -50,6 +50,9 @@ def parse_args():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--io-sweep", action="store_true",
+                    help="instead of the benchmark: forward + backward at N = 1K .. 16K, d = 128, "
+                         "B * H * N fixed, one JSON line per N with the three byte models")
     return ap.parse_args()
 
 
@@ -295,6 +298,58 @@ def copy_calibration(args, dev):
     torch.cuda.synchronize()
 
 
+IO_SWEEP_N = (1024, 2048, 4096, 8192, 16384)
+
+
+def io_sweep(args):
+    """Non-causal bf16 attention at d = 128 with B * H * N fixed at 2^19 rows
+    (H = 16): compulsory bytes stay constant over the sweep while the tile
+    model and Algorithm 0 grow in proportion to N. Prints per N the timings
+    and the byte models; the HBM bytes come from counter passes over this
+    same command (one kernel dispatch group per N, in this order)."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_29_amd as fa
+    from exact_io_aware_29_amd import accounting as acc
+
+    dev = torch.device("cuda:0")
+    d, H = 128, 16
+    for N in IO_SWEEP_N:
+        B = (1 << 19) // (H * N)
+        g = torch.Generator(device="cpu").manual_seed(N)
+        q, k, v, do = (torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+                       .to(torch.bfloat16).to(dev) for _ in range(4))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        p = fa.make_params(batch=B, heads_q=H, heads_kv=H, seqlen=N, head_dim=d)
+        ws = torch.empty(fa.fa_bwd_workspace_size(p) // 4 + 4, dtype=torch.float32, device=dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        tf, tb = [], []
+        for it in range(args.warmup + args.steps):
+            ev[0].record()
+            fa.fa_fwd(q, k, v, out=o, lse=lse)
+            ev[1].record()
+            fa.fa_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                tf.append(ev[0].elapsed_time(ev[1]))
+                tb.append(ev[1].elapsed_time(ev[2]))
+        tiles = B * H * (N // 128) ** 2
+        m = acc.bytes_models(B, H, H, N, d, 2, tiles=tiles)
+        fl = acc.flops(B * H * N * N, d)
+        print(json.dumps({"io_sweep": True, "N": N, "batch": B, "heads": H, "head_dim": d,
+                          "fwd_ms": round(float(np.median(tf)), 4),
+                          "bwd_ms": round(float(np.median(tb)), 4),
+                          "fwd_tflops": round(fl["fwd"] / (np.median(tf) * 1e-3) / 1e12, 1),
+                          "bwd_tflops": round(fl["bwd"] / (np.median(tb) * 1e-3) / 1e12, 1),
+                          "bytes_models": m}), flush=True)
+        del q, k, v, do, o, dq, dk, dv, ws
+    copy_calibration(args, dev)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -305,6 +360,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.io_sweep:
+        io_sweep(args)
+        return
 
     import exact_io_aware_29_amd as fa
     from exact_io_aware_29_amd import accounting as acc
