@@ -1,0 +1,78 @@
+"""Host-side checks of bench.py that need no GPU: the one-GPU contract, the
+CPU-baseline legs (fields, bounded time, the long-sequence row sample), the
+kernel source hashes and the recorded-traffic parser."""
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+import bench
+from synth import Workload, draw, draw_case
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _check_baseline(rec, unit):
+    assert rec["kind"] == "oracle" and rec["unit"] == unit
+    assert rec["value"] > 0 and rec["cores"] >= 1
+    assert isinstance(rec["cpu"], str) and rec["sample"]
+
+
+def test_cpu_baseline_fields_and_budget():
+    inp = draw_case(2, 2, 1, 192, 64, "bf16", causal=True, seqlens=[150, 192], seed=3)
+    per_b = [int(x) for x in (150 * 151 // 2 + 42 * 150, 192 * 193 // 2)]
+    t0 = time.perf_counter()
+    rec = bench.cpu_baseline(inp, per_b, 0.2)
+    assert time.perf_counter() - t0 < 30
+    _check_baseline(rec, "TFLOP/s")
+
+
+def test_cpu_baseline_long_sequence_samples_rows():
+    w = Workload("t", 1, 1, 1, 16384, 64, "bf16", butterfly=True)
+    inp = draw(w, 5)
+    t0 = time.perf_counter()
+    rec = bench.cpu_baseline(inp, [1], 0.5)
+    assert time.perf_counter() - t0 < 60
+    _check_baseline(rec, "TFLOP/s")
+    assert "rows of (batch 0, head 0)" in rec["sample"]
+
+
+def test_decode_cpu_baseline_fields():
+    w = Workload("t", 2, 4, 2, 512, 64, "bf16", pad_range=(100, 512), backward=False, decode=True)
+    inp = draw(w, 7)
+    rec = bench.decode_cpu_baseline(inp, 0.2)
+    _check_baseline(rec, "GB/s")
+
+
+def test_every_kernel_source_hashes():
+    for k in bench.KERNEL_SOURCES:
+        h = bench.source_hash(k)
+        assert len(h) == 16 and int(h, 16) >= 0
+
+
+def test_recorded_traffic_lines_parse():
+    """Every committed traffic line names a known kernel and a byte count;
+    recorded_traffic returns it only while the source hash still matches."""
+    import re
+    pat = re.compile(r"^traffic\s+(\S+)\s+bytes_per_launch=(\d+)\s+src=(\w+)", re.M)
+    found = 0
+    for name in os.listdir(os.path.join(ROOT, "profiles")):
+        m = re.match(r"hbm_traffic_w(\d+)\.md$", name)
+        if not m:
+            continue
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        for kernel, nbytes, src in pat.findall(text):
+            assert kernel in bench.KERNEL_SOURCES, kernel
+            got = bench.recorded_traffic(kernel, int(m.group(1)))
+            assert got == (int(nbytes) if src == bench.source_hash(kernel) else None)
+            found += 1
+    assert found > 0
