@@ -242,7 +242,7 @@ struct FwdB {
   static constexpr float kLag = 8.f;
 };
 
-template <int D, bool DROP>
+template <int D, bool DROP, int NREP>
 __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   using C = FwdB<D>;
   using T = typename C::T;
@@ -255,13 +255,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   const int lr = lane & 31, hh = lane >> 5;
 
   const int nqb = (p.N + C::BR - 1) / C::BR;
+  // Causal (NREP = 2): a workgroup takes query block nqb - 1 - i and then
+  // block i, so that every workgroup does about the same work (nqb + 1
+  // blocks of keys per pair) and the per-block prologue and epilogue are
+  // spread over twice the tiles; heaviest block first. NREP = 1: one block.
+  static_assert(NREP == 1 || NREP == 2, "one block or a pair");
+  const int nunit = NREP == 2 ? (nqb + 1) / 2 : nqb;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int head_lin = L / nqb;
-  const int qbi = L - head_lin * nqb;
-  const int qb = p.causal ? nqb - 1 - qbi : qbi;  // causal: longest rows first
+  const int head_lin = L / nunit;
+  const int ui = L - head_lin * nunit;
   const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
-  const int q0 = qb * C::BR;
-  const int my_q = q0 + 32 * w + lr;
 
   const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;  // row strides in bytes
   const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
@@ -270,197 +273,206 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
                              (uint32_t)(p.N - 1) * vsb + 2 * D);
 
   const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
-  // Keys any row of the block may see: causal / padding / right window edge
-  // bound the end, the left window edge the start.
-  const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
-  const int ntiles = (kend + C::BC - 1) / C::BC;
-  const int kfirst = max(0, q0 - p.wl) / C::BC;
+  for (int rep = 0; rep < NREP; ++rep) {
+    const int qb = NREP == 2 ? (rep == 0 ? nqb - 1 - ui : ui) : ui;
+    if (rep == 1) {
+      if (qb == nqb - 1 - ui) break;  // the middle block of an odd count
+      __syncthreads();  // the first block's last tile is no longer read
+    }
+    const int q0 = qb * C::BR;
+    const int my_q = q0 + 32 * w + lr;
+    // Keys any row of the block may see: causal / padding / right window edge
+    // bound the end, the left window edge the start.
+    const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
+    const int ntiles = (kend + C::BC - 1) / C::BC;
+    const int kfirst = max(0, q0 - p.wl) / C::BC;
 
-  bf16x8 qf[C::NKK];
-  {
-    const bool ok = my_q < p.N;
-    const bf16* qrow = static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h +
-                       (int64_t)(ok ? my_q : 0) * a.sq.n + 8 * hh;
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = frag_g(qrow + 16 * kk, ok);
-  }
-
-  int kvo[T::NLD], vvo[T::NLD];
-  dma_offsets<D, C::BC>(kvo, ksb, w, lane);
-  dma_offsets<D, C::BC>(vvo, vsb, w, lane);
-  int roff[C::NKK], troff[C::NDB][2];
-  row_offsets<D, C::BC>(roff, lr, hh);
-  tr_offsets<D, C::BC>(troff, lane);
-
-  f32x16 acc[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
-  float m_ref = -kInf;  // exponent reference of this lane's row (log2 units)
-  float l_run = 0.f;    // this lane half's share of the row's exp-sum
-  const float sl2 = p.scale_l2;
-  const int64_t log_row =
-      a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
-
-  auto next_visit = [&](int kt) {
-    while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
-    return kt;
-  };
-  auto issue = [&](int kt, char* stage) {
-    dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
-    dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
-  };
-
-  int kt = next_visit(kfirst);
-  if (kt < ntiles) {
-    issue(kt, smem[0]);
-    wait_dma();
-    __syncthreads();
-  }
-  // One key tile, read from stage `Ks` while the next visited tile lands in
-  // `fill`. The two restrict-qualified stages tell the compiler that these
-  // reads never alias that DMA, so it does not make the transposing reads
-  // wait for the DMA to land.
-  auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
-    const char* Vs = Ks + T::BYTES;
-    const int key0 = kt * C::BC;
-    const int nxt = next_visit(kt + 1);
-    if (nxt < ntiles) issue(nxt, fill);  // lands while this tile is computed
-    if (a.log && tid == 0) log_tile(a.log, log_row, key0);
-    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
-                           (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
-
-    // One straight-line block per tile (no per-sub-tile branches), so the
-    // compiler can overlap one sub-tile's exponentials with its neighbour's
-    // matrix products: all S^T products, one max and lazy-rescale test for
-    // the whole tile, then exp / pack / PV per sub-tile.
-    f32x16 s[C::NSUB];
-    // Raised priority while this wave feeds the matrix pipe, so that waves
-    // sharing the SIMD fill the VALU between its products.
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int t = 0; t < C::NSUB; ++t) s[t] = f32x16{};
-    // Head-dim steps outer, sub-tiles inner: the sub-tiles' accumulation
-    // chains interleave.
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk)
-#pragma unroll
-      for (int t = 0; t < C::NSUB; ++t)
-        s[t] = mfma(lds_row(Ks + 32 * t * T::RB, roff[kk]), qf[kk], s[t]);
+    bf16x8 qf[C::NKK];
     {
-      // Keep four operand fragments in flight ahead of the products.
-      constexpr int NM = C::NSUB * C::NKK;
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      const bool ok = my_q < p.N;
+      const bf16* qrow = static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h +
+                         (int64_t)(ok ? my_q : 0) * a.sq.n + 8 * hh;
 #pragma unroll
-      for (int i = 0; i < NM - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      for (int kk = 0; kk < C::NKK; ++kk) qf[kk] = frag_g(qrow + 16 * kk, ok);
     }
-    __builtin_amdgcn_s_setprio(0);
-    if (__builtin_expect(need_mask, false)) {  // boundary tiles only
-      // Key j is seen iff my_q - wl <= j <= my_q + hi (hi = 0 under the
-      // causal mask, else the right window edge) and j < kvalid; the band
-      // test is one unsigned compare of j - my_q + wl against wl + hi.
-      const unsigned hi = p.causal ? 0u : (unsigned)p.wr;
-      const unsigned span = (unsigned)p.wl + hi;
-      const unsigned base = (unsigned)(key0 + 8 * hh + p.wl) - (unsigned)my_q;
+
+    int kvo[T::NLD], vvo[T::NLD];
+    dma_offsets<D, C::BC>(kvo, ksb, w, lane);
+    dma_offsets<D, C::BC>(vvo, vsb, w, lane);
+    int roff[C::NKK], troff[C::NDB][2];
+    row_offsets<D, C::BC>(roff, lr, hh);
+    tr_offsets<D, C::BC>(troff, lane);
+
+    f32x16 acc[C::NDB];
 #pragma unroll
-      for (int t = 0; t < C::NSUB; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * t + perm_row(r, hh);
-          const bool kill =
-              (base + (unsigned)(32 * t + perm_row(r, 0)) > span) | (key >= kvalid);
-          s[t][r] = kill ? -kInf : s[t][r];  // branch-free select
-        }
+    for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+    float m_ref = -kInf;  // exponent reference of this lane's row (log2 units)
+    float l_run = 0.f;    // this lane half's share of the row's exp-sum
+    const float sl2 = p.scale_l2;
+    const int64_t log_row =
+        a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+
+    auto next_visit = [&](int kt) {
+      while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
+      return kt;
+    };
+    auto issue = [&](int kt, char* stage) {
+      dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
+      dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
+    };
+
+    int kt = next_visit(kfirst);
+    if (kt < ntiles) {
+      issue(kt, smem[0]);
+      wait_dma();
+      __syncthreads();
     }
-    float mx = tree_max16(s[0]);
-#pragma unroll
-    for (int t = 1; t < C::NSUB; ++t) mx = fmaxf(mx, tree_max16(s[t]));
-    mx = half_max(mx) * sl2;
-    if (wave_any(mx > m_ref + C::kLag)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    }
-    const float m_use = m_ref == -kInf ? 0.f : m_ref;
-#pragma unroll
-    for (int t = 0; t < C::NSUB; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, -m_use));
-      l_run += tree_sum16(s[t]);
-      if constexpr (DROP) {  // zero dropped entries after they entered l
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          drop_run8(s[t], 8 * c,
-                    drop_bits(p, (uint32_t)(key0 + 32 * t + 16 * c + 8 * hh) >> 3,
-                              (uint32_t)my_q, (uint32_t)(b * p.Hq + h)),
-                    p.drop_thr);
-      }
+    // One key tile, read from stage `Ks` while the next visited tile lands in
+    // `fill`. The two restrict-qualified stages tell the compiler that these
+    // reads never alias that DMA, so it does not make the transposing reads
+    // wait for the DMA to land.
+    auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
+      const char* Vs = Ks + T::BYTES;
+      const int key0 = kt * C::BC;
+      const int nxt = next_visit(kt + 1);
+      if (nxt < ntiles) issue(nxt, fill);  // lands while this tile is computed
+      if (a.log && tid == 0) log_tile(a.log, log_row, key0);
+      const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
+                             (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
+
+      // One straight-line block per tile (no per-sub-tile branches), so the
+      // compiler can overlap one sub-tile's exponentials with its neighbour's
+      // matrix products: all S^T products, one max and lazy-rescale test for
+      // the whole tile, then exp / pack / PV per sub-tile.
+      f32x16 s[C::NSUB];
+      // Raised priority while this wave feeds the matrix pipe, so that waves
+      // sharing the SIMD fill the VALU between its products.
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 pf = pack8(s[t], c);
-        const char* vp = Vs + (32 * t + 16 * c) * T::RB;
+      for (int t = 0; t < C::NSUB; ++t) s[t] = f32x16{};
+      // Head-dim steps outer, sub-tiles inner: the sub-tiles' accumulation
+      // chains interleave.
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          acc[db] = mfma(lds_tr(vp, troff[db][0], troff[db][1]), pf, acc[db]);
-      }
+      for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+        for (int t = 0; t < C::NSUB; ++t)
+          s[t] = mfma(lds_row(Ks + 32 * t * T::RB, roff[kk]), qf[kk], s[t]);
       {
-        // Transposing reads of four operands in flight ahead of the products.
-        constexpr int NM = 2 * C::NDB;
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        // Keep four operand fragments in flight ahead of the products.
+        constexpr int NM = C::NSUB * C::NKK;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int i = 0; i < NM - 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       __builtin_amdgcn_s_setprio(0);
-    }
-    if (nxt < ntiles) {
-      wait_dma();
-      __syncthreads();  // next tile landed everywhere; this tile is no longer read
-    }
-    kt = nxt;
-  };
-  for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
-
-  const float l_tot = half_sum(l_run);
-  const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;
-  if (my_q < p.N) {
-    char* obase = static_cast<char*>(a.o);
-    const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n;
+      if (__builtin_expect(need_mask, false)) {  // boundary tiles only
+        // Key j is seen iff my_q - wl <= j <= my_q + hi (hi = 0 under the
+        // causal mask, else the right window edge) and j < kvalid; the band
+        // test is one unsigned compare of j - my_q + wl against wl + hi.
+        const unsigned hi = p.causal ? 0u : (unsigned)p.wr;
+        const unsigned span = (unsigned)p.wl + hi;
+        const unsigned base = (unsigned)(key0 + 8 * hh + p.wl) - (unsigned)my_q;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+        for (int t = 0; t < C::NSUB; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * hh;
-        const float v0 = acc[db][4 * g] * inv, v1 = acc[db][4 * g + 1] * inv;
-        const float v2 = acc[db][4 * g + 2] * inv, v3 = acc[db][4 * g + 3] * inv;
-        if (a.o_fp32) {
-          *reinterpret_cast<float4*>(obase + (orow + d0) * 4) = make_float4(v0, v1, v2, v3);
-        } else {
-          bf16x4 pk;
-          pk[0] = (bf16)v0;
-          pk[1] = (bf16)v1;
-          pk[2] = (bf16)v2;
-          pk[3] = (bf16)v3;
-          *reinterpret_cast<bf16x4*>(obase + (orow + d0) * 2) = pk;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * t + perm_row(r, hh);
+            const bool kill =
+                (base + (unsigned)(32 * t + perm_row(r, 0)) > span) | (key >= kvalid);
+            s[t][r] = kill ? -kInf : s[t][r];  // branch-free select
+          }
       }
-    if (hh == 0) {
-      const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -kInf;
-      a.lse[((int64_t)b * p.Hq + h) * p.N + my_q] = lse;
+      float mx = tree_max16(s[0]);
+#pragma unroll
+      for (int t = 1; t < C::NSUB; ++t) mx = fmaxf(mx, tree_max16(s[t]));
+      mx = half_max(mx) * sl2;
+      if (wave_any(mx > m_ref + C::kLag)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      }
+      const float m_use = m_ref == -kInf ? 0.f : m_ref;
+#pragma unroll
+      for (int t = 0; t < C::NSUB; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], sl2, -m_use));
+        l_run += tree_sum16(s[t]);
+        if constexpr (DROP) {  // zero dropped entries after they entered l
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            drop_run8(s[t], 8 * c,
+                      drop_bits(p, (uint32_t)(key0 + 32 * t + 16 * c + 8 * hh) >> 3,
+                                (uint32_t)my_q, (uint32_t)(b * p.Hq + h)),
+                      p.drop_thr);
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 pf = pack8(s[t], c);
+          const char* vp = Vs + (32 * t + 16 * c) * T::RB;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            acc[db] = mfma(lds_tr(vp, troff[db][0], troff[db][1]), pf, acc[db]);
+        }
+        {
+          // Transposing reads of four operands in flight ahead of the products.
+          constexpr int NM = 2 * C::NDB;
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int i = 0; i < NM - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+      if (nxt < ntiles) {
+        wait_dma();
+        __syncthreads();  // next tile landed everywhere; this tile is no longer read
+      }
+      kt = nxt;
+    };
+    for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
+
+    const float l_tot = half_sum(l_run);
+    const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;
+    if (my_q < p.N) {
+      char* obase = static_cast<char*>(a.o);
+      const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * hh;
+          const float v0 = acc[db][4 * g] * inv, v1 = acc[db][4 * g + 1] * inv;
+          const float v2 = acc[db][4 * g + 2] * inv, v3 = acc[db][4 * g + 3] * inv;
+          if (a.o_fp32) {
+            *reinterpret_cast<float4*>(obase + (orow + d0) * 4) = make_float4(v0, v1, v2, v3);
+          } else {
+            bf16x4 pk;
+            pk[0] = (bf16)v0;
+            pk[1] = (bf16)v1;
+            pk[2] = (bf16)v2;
+            pk[3] = (bf16)v3;
+            *reinterpret_cast<bf16x4*>(obase + (orow + d0) * 2) = pk;
+          }
+        }
+      if (hh == 0) {
+        const float lse = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -kInf;
+        a.lse[((int64_t)b * p.Hq + h) * p.N + my_q] = lse;
+      }
     }
-  }
+  }  // q-blocks of this workgroup
 }
 
 // fp32 inputs (reference-precision path) use the generic kernel above.
@@ -475,11 +487,19 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
 template <int D>
 static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const int64_t nqb = (a.p.N + FwdB<D>::BR - 1) / FwdB<D>::BR;
-  const int64_t grid = nqb * a.p.Hq * a.p.B;
-  if (a.p.drop)
-    hipLaunchKernelGGL((fwd_kernel_bf16<D, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel_bf16<D, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  const dim3 blk(256);
+  // Pairs of query blocks where the work per block grows with the block
+  // index (causal, no left window edge); under a sliding window every block
+  // already does about the same work.
+  if (a.p.causal && a.p.wl >= a.p.N) {
+    const dim3 g((unsigned)(((nqb + 1) / 2) * a.p.Hq * a.p.B));
+    if (a.p.drop) hipLaunchKernelGGL((fwd_kernel_bf16<D, true, 2>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel_bf16<D, false, 2>), g, blk, 0, s, a);
+  } else {
+    const dim3 g((unsigned)(nqb * a.p.Hq * a.p.B));
+    if (a.p.drop) hipLaunchKernelGGL((fwd_kernel_bf16<D, true, 1>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel_bf16<D, false, 1>), g, blk, 0, s, a);
+  }
   return hipGetLastError();
 }
 
