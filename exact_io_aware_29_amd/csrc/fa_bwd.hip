@@ -388,7 +388,7 @@ struct DqCfg {
   using T = SwzTile<D, BC>;
 };
 
-template <int D, bool DROP>
+template <int D, bool DROP, int NREP>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D>;
   using T = typename C::T;
@@ -401,13 +401,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
   const int nqb = (p.N + C::BR - 1) / C::BR;
+  // NREP = 2 (causal, no left window edge): query blocks nqb - 1 - i and i in
+  // one workgroup, heaviest first, as in the forward.
+  static_assert(NREP == 1 || NREP == 2, "one block or a pair");
+  const int nunit = NREP == 2 ? (nqb + 1) / 2 : nqb;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int head_lin = L / nqb;
-  const int qbi = L - head_lin * nqb;
-  const int qb = p.causal ? nqb - 1 - qbi : qbi;
+  const int head_lin = L / nunit;
+  const int ui = L - head_lin * nunit;
   const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
-  const int q0 = qb * C::BR;
-  const int my_q = q0 + 32 * w + lr;
   const float sl2 = p.scale_l2;
   const bool causal = p.causal != 0;
 
@@ -416,178 +417,187 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
                              (uint32_t)(p.N - 1) * ksb + 2 * D);
   const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
                              (uint32_t)(p.N - 1) * vsb + 2 * D);
-
-  const bool qok = my_q < p.N;
-  bf16x8 qf[C::NKK], dof[C::NKK];
-  {
-    const int64_t r = qok ? my_q : 0;
-    const bf16* Qp = static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h + r * a.sq.n + 8 * hh;
-    const bf16* dOp = static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h + r * a.sdo.n + 8 * hh;
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) {
-      qf[kk] = frag_g(Qp + 16 * kk, qok);
-      dof[kk] = frag_g(dOp + 16 * kk, qok);
+  for (int rep = 0; rep < NREP; ++rep) {
+    const int qb = NREP == 2 ? (rep == 0 ? nqb - 1 - ui : ui) : (causal ? nqb - 1 - ui : ui);
+    if (rep == 1) {
+      if (qb == nqb - 1 - ui) break;  // the middle block of an odd count
+      __syncthreads();  // the first block's last tile is no longer read
     }
-  }
-  // Row statistics of this lane's row, computed here and stored for the
-  // dK/dV kernel, which runs after this one: D = dO . O (the two lane halves
-  // hold interleaved halves of the row), q D under dropout (with
-  // dP = (Z / q) o dO V^T, dS = P o (dP - D) = (1 / q) P o (Z o dO V^T - q D),
-  // and the 1 / q joins the final scales), and the LSE in base-2 units
-  // (+inf for a row with no allowed key, so that every rebuilt probability
-  // of it is 2^-inf = 0).
-  const int64_t rowstat = ((int64_t)b * p.Hq + h) * p.N + (qok ? my_q : 0);
-  float dpart = 0.f;
-  if (qok) {
-    const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n + 8 * hh;
+    const int q0 = qb * C::BR;
+    const int my_q = q0 + 32 * w + lr;
+
+    const bool qok = my_q < p.N;
+    bf16x8 qf[C::NKK], dof[C::NKK];
+    {
+      const int64_t r = qok ? my_q : 0;
+      const bf16* Qp = static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h + r * a.sq.n + 8 * hh;
+      const bf16* dOp = static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h + r * a.sdo.n + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) {
-      float o8[8];
-      if (a.o_fp32) {
-        const float* op = static_cast<const float*>(a.o) + orow + 16 * kk;
-        const float4 x0 = *reinterpret_cast<const float4*>(op);
-        const float4 x1 = *reinterpret_cast<const float4*>(op + 4);
-        o8[0] = x0.x; o8[1] = x0.y; o8[2] = x0.z; o8[3] = x0.w;
-        o8[4] = x1.x; o8[5] = x1.y; o8[6] = x1.z; o8[7] = x1.w;
-      } else {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.o) + orow + 16 * kk);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] = (float)x[e];
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        qf[kk] = frag_g(Qp + 16 * kk, qok);
+        dof[kk] = frag_g(dOp + 16 * kk, qok);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[kk][e], o8[e], dpart);
     }
-  }
-  const float dsum = half_sum(dpart);
-  const float dq_d = p.drop ? dsum * p.drop_q : dsum;
-  const float lse2 = qok ? lse2_of(a.lse[rowstat]) : kInf;
-  if (qok && hh == 0) {
-    a.dvec[rowstat] = dq_d;
-    a.lse2[rowstat] = lse2;
-  }
-
-  int kvo[T::NLD], vvo[T::NLD];
-  dma_offsets<D, C::BC>(kvo, ksb, w, lane);
-  dma_offsets<D, C::BC>(vvo, vsb, w, lane);
-  int roff[C::NKK], troff[C::NDB][2];
-  row_offsets<D, C::BC>(roff, lr, hh);
-  tr_offsets<D, C::BC>(troff, lane);
-
-  f32x16 acc[C::NDB];
+    // Row statistics of this lane's row, computed here and stored for the
+    // dK/dV kernel, which runs after this one: D = dO . O (the two lane halves
+    // hold interleaved halves of the row), q D under dropout (with
+    // dP = (Z / q) o dO V^T, dS = P o (dP - D) = (1 / q) P o (Z o dO V^T - q D),
+    // and the 1 / q joins the final scales), and the LSE in base-2 units
+    // (+inf for a row with no allowed key, so that every rebuilt probability
+    // of it is 2^-inf = 0).
+    const int64_t rowstat = ((int64_t)b * p.Hq + h) * p.N + (qok ? my_q : 0);
+    float dpart = 0.f;
+    if (qok) {
+      const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)my_q * a.so.n + 8 * hh;
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
-
-  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
-  const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
-  const int ntiles = (kend + C::BC - 1) / C::BC;
-  const int64_t log_row =
-      a.log_q ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
-  auto next_visit = [&](int kt) {
-    while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
-    return kt;
-  };
-  auto issue = [&](int kt, char* stage) {
-    dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
-    dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
-  };
-
-  int kt = next_visit(max(0, q0 - p.wl) / C::BC);
-  if (kt < ntiles) {
-    issue(kt, smem[0]);
-    wait_dma();
-    __syncthreads();
-  }
-  // One key tile read from stage `Ks` while the next lands in `fill`
-  // (restrict-qualified: these reads never wait for that DMA).
-  auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
-    const char* Vs = Ks + T::BYTES;
-    const int key0 = kt * C::BC;
-    const int nxt = next_visit(kt + 1);
-    if (nxt < ntiles) issue(nxt, fill);
-    if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
-    const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
-                           (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        float o8[8];
+        if (a.o_fp32) {
+          const float* op = static_cast<const float*>(a.o) + orow + 16 * kk;
+          const float4 x0 = *reinterpret_cast<const float4*>(op);
+          const float4 x1 = *reinterpret_cast<const float4*>(op + 4);
+          o8[0] = x0.x; o8[1] = x0.y; o8[2] = x0.z; o8[3] = x0.w;
+          o8[4] = x1.x; o8[5] = x1.y; o8[6] = x1.z; o8[7] = x1.w;
+        } else {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.o) + orow + 16 * kk);
 #pragma unroll
-    for (int t = 0; t < C::NSUB; ++t) {
-      f32x16 st = f32x16{}, dpt = f32x16{};
-      const char* kp = Ks + 32 * t * T::RB;
-      const char* vp = Vs + 32 * t * T::RB;
-      // Raised priority while this wave feeds the matrix pipe, so that the
-      // other wave on the SIMD fills the VALU between its products.
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int k4 = 0; k4 < C::NKK; k4 += 4) {
-        bf16x8 ka[4], va[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ka[i] = lds_row(kp, roff[k4 + i]);
-          va[i] = lds_row(vp, roff[k4 + i]);
+          for (int e = 0; e < 8; ++e) o8[e] = (float)x[e];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          st = mfma(ka[i], qf[k4 + i], st);
-          dpt = mfma(va[i], dof[k4 + i], dpt);
-        }
+        for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[kk][e], o8[e], dpart);
       }
-      __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
-      if (__builtin_expect(need_mask, false)) {  // boundary tiles only
-        // Key j is seen iff my_q - wl <= j <= my_q + hi (hi = 0 under the
-        // causal mask, else the right window edge) and j < kvalid; the band
-        // test is one unsigned compare of j - my_q + wl against wl + hi.
-        const unsigned hi = causal ? 0u : (unsigned)p.wr;
-        const unsigned span = (unsigned)p.wl + hi;
-        const unsigned base = (unsigned)(key0 + 32 * t + 8 * hh + p.wl) - (unsigned)my_q;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * t + perm_row(r, hh);
-          const bool kill = (base + (unsigned)perm_row(r, 0) > span) | (key >= kvalid);
-          st[r] = kill ? 0.f : st[r];  // branch-free select
-        }
-      }
-      if constexpr (DROP) {  // dP~ of dropped entries is zero (dq_d holds q D)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          drop_run8(dpt, 8 * c,
-                    drop_bits(p, (uint32_t)(key0 + 32 * t + 16 * c + 8 * hh) >> 3,
-                              (uint32_t)my_q, (uint32_t)(b * p.Hq + h)),
-                    p.drop_thr);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (dpt[r] - dq_d);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 dsf = pack8(dpt, c);
-        const char* ktp = Ks + (32 * t + 16 * c) * T::RB;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          acc[db] = mfma(lds_tr(ktp, troff[db][0], troff[db][1]), dsf, acc[db]);
-      }
-      __builtin_amdgcn_s_setprio(0);
     }
-    if (nxt < ntiles) {
+    const float dsum = half_sum(dpart);
+    const float dq_d = p.drop ? dsum * p.drop_q : dsum;
+    const float lse2 = qok ? lse2_of(a.lse[rowstat]) : kInf;
+    if (qok && hh == 0) {
+      a.dvec[rowstat] = dq_d;
+      a.lse2[rowstat] = lse2;
+    }
+
+    int kvo[T::NLD], vvo[T::NLD];
+    dma_offsets<D, C::BC>(kvo, ksb, w, lane);
+    dma_offsets<D, C::BC>(vvo, vsb, w, lane);
+    int roff[C::NKK], troff[C::NDB][2];
+    row_offsets<D, C::BC>(roff, lr, hh);
+    tr_offsets<D, C::BC>(troff, lane);
+
+    f32x16 acc[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+
+    const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
+    const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
+    const int ntiles = (kend + C::BC - 1) / C::BC;
+    const int64_t log_row =
+        a.log_q ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+    auto next_visit = [&](int kt) {
+      while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
+      return kt;
+    };
+    auto issue = [&](int kt, char* stage) {
+      dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
+      dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
+    };
+
+    int kt = next_visit(max(0, q0 - p.wl) / C::BC);
+    if (kt < ntiles) {
+      issue(kt, smem[0]);
       wait_dma();
       __syncthreads();
     }
-    kt = nxt;
-  };
-  for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
-
-  const float qscale = DROP ? p.scale * p.drop_scale : p.scale;
-  if (qok) {
-    bf16* dqp = static_cast<bf16*>(a.dq) + b * a.sdq.b + h * a.sdq.h + (int64_t)my_q * a.sdq.n;
+    // One key tile read from stage `Ks` while the next lands in `fill`
+    // (restrict-qualified: these reads never wait for that DMA).
+    auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
+      const char* Vs = Ks + T::BYTES;
+      const int key0 = kt * C::BC;
+      const int nxt = next_visit(kt + 1);
+      if (nxt < ntiles) issue(nxt, fill);
+      if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
+      const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
+                             (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+      for (int t = 0; t < C::NSUB; ++t) {
+        f32x16 st = f32x16{}, dpt = f32x16{};
+        const char* kp = Ks + 32 * t * T::RB;
+        const char* vp = Vs + 32 * t * T::RB;
+        // Raised priority while this wave feeds the matrix pipe, so that the
+        // other wave on the SIMD fills the VALU between its products.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v;
+        for (int k4 = 0; k4 < C::NKK; k4 += 4) {
+          bf16x8 ka[4], va[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[db][4 * g + e] * qscale);
-        *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * g + 4 * hh) = v;
+          for (int i = 0; i < 4; ++i) {
+            ka[i] = lds_row(kp, roff[k4 + i]);
+            va[i] = lds_row(vp, roff[k4 + i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            st = mfma(ka[i], qf[k4 + i], st);
+            dpt = mfma(va[i], dof[k4 + i], dpt);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
+        if (__builtin_expect(need_mask, false)) {  // boundary tiles only
+          // Key j is seen iff my_q - wl <= j <= my_q + hi (hi = 0 under the
+          // causal mask, else the right window edge) and j < kvalid; the band
+          // test is one unsigned compare of j - my_q + wl against wl + hi.
+          const unsigned hi = causal ? 0u : (unsigned)p.wr;
+          const unsigned span = (unsigned)p.wl + hi;
+          const unsigned base = (unsigned)(key0 + 32 * t + 8 * hh + p.wl) - (unsigned)my_q;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * t + perm_row(r, hh);
+            const bool kill = (base + (unsigned)perm_row(r, 0) > span) | (key >= kvalid);
+            st[r] = kill ? 0.f : st[r];  // branch-free select
+          }
+        }
+        if constexpr (DROP) {  // dP~ of dropped entries is zero (dq_d holds q D)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            drop_run8(dpt, 8 * c,
+                      drop_bits(p, (uint32_t)(key0 + 32 * t + 16 * c + 8 * hh) >> 3,
+                                (uint32_t)my_q, (uint32_t)(b * p.Hq + h)),
+                      p.drop_thr);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (dpt[r] - dq_d);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 dsf = pack8(dpt, c);
+          const char* ktp = Ks + (32 * t + 16 * c) * T::RB;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            acc[db] = mfma(lds_tr(ktp, troff[db][0], troff[db][1]), dsf, acc[db]);
+        }
+        __builtin_amdgcn_s_setprio(0);
       }
-  }
+      if (nxt < ntiles) {
+        wait_dma();
+        __syncthreads();
+      }
+      kt = nxt;
+    };
+    for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
+
+    const float qscale = DROP ? p.scale * p.drop_scale : p.scale;
+    if (qok) {
+      bf16* dqp = static_cast<bf16*>(a.dq) + b * a.sdq.b + h * a.sdq.h + (int64_t)my_q * a.sdq.n;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[db][4 * g + e] * qscale);
+          *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * g + 4 * hh) = v;
+        }
+    }
+  }  // query blocks of this workgroup
 }
 
 // ----------------------------------------------------------------- launchers
@@ -607,14 +617,23 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t grid = (int64_t)((a.p.N + 127) / 128) * a.p.Hq * a.p.B;
-  const dim3 g((unsigned)grid), blk(256);
+  const dim3 blk(256);
+  // Pairs of query blocks where the causal work grows with the block index.
+  const bool pair = a.p.causal && a.p.wl >= a.p.N;
+  const dim3 g((unsigned)(pair ? ((a.p.N + 127) / 128 + 1) / 2 * a.p.Hq * a.p.B : grid));
+#define FA_DQ_LAUNCH(DD, DR)                                                             \
+  do {                                                                                   \
+    if (pair) hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 2>), g, blk, 0, s, a);           \
+    else hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 1>), g, blk, 0, s, a);                \
+  } while (0)
   if (head_dim == 64) {
-    if (a.p.drop) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<64, false>), g, blk, 0, s, a);
+    if (a.p.drop) FA_DQ_LAUNCH(64, true);
+    else FA_DQ_LAUNCH(64, false);
   } else {
-    if (a.p.drop) hipLaunchKernelGGL((bwd_dq_kernel<128, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), g, blk, 0, s, a);
+    if (a.p.drop) FA_DQ_LAUNCH(128, true);
+    else FA_DQ_LAUNCH(128, false);
   }
+#undef FA_DQ_LAUNCH
   return hipGetLastError();
 }
 
