@@ -34,6 +34,44 @@ __device__ __forceinline__ float lse2_of(float lse) {
   return lse == -kInf ? kInf : lse * kLog2e;
 }
 
+// A row value as the starting accumulator of a product chain. The output
+// of a 32 x 32 product keeps 16 rows per lane, so subtracting a per-row
+// value there would need those 16 values in every lane (eight 16-byte LDS
+// reads per sub-tile for LSE and D). Instead one extra product broadcasts
+// it: lane i of the A operand holds its row's value c split exactly into
+// three bf16 terms (two truncations, then the rounded rest: c to within
+// 2^-23 |c|) in K slots 0..2, and a constant B operand with -1 in those
+// slots makes every output of row i equal to -c. Lane half 0 carries one
+// value (row LSE) and lane half 1 another (row D), which the two B
+// constants select: K slots 0..2 are lane half 0's, slots 8..10 half 1's.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct f32x4x4 {
+  f32x4 v[4];
+};
+
+__device__ __forceinline__ bf16x8 split3_frag(float c) {
+  const uint32_t hi = __float_as_uint(c) & 0xffff0000u;
+  const float r1 = c - __uint_as_float(hi);
+  const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
+  const float lo = r1 - __uint_as_float(mid);
+  u32x4 w;
+  w[0] = (hi >> 16) | mid;
+  w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo);
+  w[2] = 0u;
+  w[3] = 0u;
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// -1 in K slots 0..2 of lane half `half`, zero elsewhere.
+__device__ __forceinline__ bf16x8 neg_ones_frag(int hh, int half) {
+  u32x4 w;
+  w[0] = hh == half ? 0xBF80BF80u : 0u;
+  w[1] = hh == half ? 0x0000BF80u : 0u;
+  w[2] = 0u;
+  w[3] = 0u;
+  return __builtin_bit_cast(bf16x8, w);
+}
+
 // ----------------------------------------------------------------- dK, dV
 
 template <int D>
@@ -50,6 +88,11 @@ struct DkdvCfg {
   static constexpr int FB = D == 64 ? 4 : 2;     // operand fragments fetched per batch
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
+  // Row statistics enter as chain starts (one product per chain) instead of
+  // per-register LDS reads: at d=64, 31 fewer LDS reads per step against 8
+  // more products; at d=128 (one sub-tile per step) the saving is 7 reads
+  // and the extra registers would spill.
+  static constexpr bool FOLD = D == 64;
   using T = SwzTile<D, BQ>;
   using VT = SwzTile<D, BK>;
   // One stage: Q tile | dO tile | log2-domain LSE of its rows | D of its
@@ -249,13 +292,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       // one uniform mask block, then P / dS and the dV, dK products, so the
       // compiler can overlap one sub-tile's exponentials with another's
       // matrix products.
+      // FOLD: row statistics as chain starts. Lane half 0 reads LSE log2e /
+      // (scale log2e) of its A-operand row (clamped: an empty row's +inf
+      // becomes a finite value whose probabilities still underflow to 0),
+      // half 1 the row's D. S then starts at -LSE / scale and dP at -D
+      // (without dropout; with it dP starts at 0 and D is applied per
+      // element). Otherwise the 16 per-register values are read from LDS.
+      const float* stat_row = reinterpret_cast<const float*>(
+                                  Qs + ((lane >> 5) ? C::DVEC_OFF : C::LSE_OFF)) +
+                              swap_bits23(lr);
+      const float stat_mul = hh ? 1.f : 1.f / sl2;
+      auto row_stats = [&](int off, int u) {  // the 16 values of sub-tile u
+        const f32x4* v4 = reinterpret_cast<const f32x4*>(Qs + off) + 8 * u + 2 * hh;
+        return f32x4x4{v4[0], v4[1], v4[4], v4[5]};
+      };
 #pragma unroll
       for (int g0 = 0; g0 < C::NQS; g0 += C::NG) {
         f32x16 s[C::NG], dp[C::NG];
 #pragma unroll
         for (int uu = 0; uu < C::NG; ++uu) {
-          s[uu] = f32x16{};
-          dp[uu] = f32x16{};
+          if constexpr (C::FOLD) {
+            const bf16x8 cf = split3_frag(fminf(stat_row[32 * (g0 + uu)] * stat_mul, 1e30f));
+            s[uu] = mfma(cf, neg_ones_frag(hh, 0), f32x16{});
+            dp[uu] = DROP ? f32x16{} : mfma(cf, neg_ones_frag(hh, 1), f32x16{});
+          } else {
+            s[uu] = f32x16{};
+            dp[uu] = f32x16{};
+          }
           const char* qp = Qs + 32 * (g0 + uu) * T::RB;
           const char* dop = dOs + 32 * (g0 + uu) * T::RB;
 #pragma unroll
@@ -278,12 +341,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         // Register r of sub-tile u holds query row 32u + perm_row(r, hh).
 #pragma unroll
         for (int uu = 0; uu < C::NG; ++uu) {
-          const f32x4* l4 =
-              reinterpret_cast<const f32x4*>(Qs + C::LSE_OFF) + 8 * (g0 + uu) + 2 * hh;
-          const f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
+          if constexpr (C::FOLD) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[uu][r] = __builtin_amdgcn_exp2f(fmaf(s[uu][r], sl2, -lv[r >> 2][r & 3]));
+            for (int r = 0; r < 16; ++r) s[uu][r] = __builtin_amdgcn_exp2f(s[uu][r] * sl2);
+          } else {
+            const f32x4x4 lv = row_stats(C::LSE_OFF, g0 + uu);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              s[uu][r] = __builtin_amdgcn_exp2f(fmaf(s[uu][r], sl2, -lv.v[r >> 2][r & 3]));
+          }
         }
         if (__builtin_expect(need_mask, false)) {  // boundary tiles only
           // Row qi sees key my_k iff qi - wl <= my_k <= qi + hi (hi = 0 under
@@ -310,10 +376,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int uu = 0; uu < C::NG; ++uu) {
-          const f32x4* d4 =
-              reinterpret_cast<const f32x4*>(Qs + C::DVEC_OFF) + 8 * (g0 + uu) + 2 * hh;
-          const f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
           if constexpr (DROP) {
+            const f32x4x4 dv = row_stats(C::DVEC_OFF, g0 + uu);
             const uint32_t bits = dbits[g0 + uu];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -323,12 +387,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
               const float pz = __int_as_float(__float_as_int(s[uu][r]) & m);
               // dS' = P (Z dP~ - q D) = (P o Z) dP~ - P (q D)  (the D row
               // vector holds q D); P o Z also feeds dV.
-              dp[uu][r] = fmaf(pz, dp[uu][r], -s[uu][r] * dv4[r >> 2][r & 3]);
+              dp[uu][r] = fmaf(pz, dp[uu][r], -s[uu][r] * dv.v[r >> 2][r & 3]);
               s[uu][r] = pz;
             }
-          } else {
+          } else if constexpr (C::FOLD) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * (dp[uu][r] - dv4[r >> 2][r & 3]);
+            for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * dp[uu][r];  // dP started at -D
+          } else {
+            const f32x4x4 dv = row_stats(C::DVEC_OFF, g0 + uu);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * (dp[uu][r] - dv.v[r >> 2][r & 3]);
           }
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
