@@ -107,7 +107,7 @@ struct DkdvCfg {
   static_assert(STAGE % 256 == 0, "stages keep the 256-byte bank period");
 };
 
-template <int D, bool DROP>
+template <int D, bool DROP, int NREP>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<D>;
   using T = typename C::T;
@@ -122,326 +122,340 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
   const int nkb = (p.N + C::BK - 1) / C::BK;
+  // Causal (NREP = 2): a workgroup takes key block i and then block
+  // nkb - 1 - i, so that every workgroup sees about the same number of
+  // query rows (the heaviest block first). NREP = 1: one block, in order of
+  // decreasing work under the causal mask (low key blocks carry the most
+  // rows).
+  static_assert(NREP == 1 || NREP == 2, "one block or a pair");
+  const int nunit = NREP == 2 ? (nkb + 1) / 2 : nkb;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int head_lin = L / nkb;
-  const int kb = L - head_lin * nkb;  // causal: low key blocks carry the most rows
+  const int head_lin = L / nunit;
+  const int ui = L - head_lin * nunit;
   const int b = head_lin / p.Hkv, hk = head_lin - b * p.Hkv;
-  const int k0 = kb * C::BK;
-  const int my_k = k0 + 32 * w + lr;
-  const float sl2 = p.scale_l2;
-  const bool causal = p.causal != 0;
-
-  const bf16* Kp = static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h;
-  const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
-
-  // This lane's key as the B operand of S = Q K^T and dP = dO V^T (V from
-  // LDS at d=128).
-  bf16x8 kf[C::NKK], vf[C::VLDS ? 1 : C::NKK];
-  {
-    const bool ok = my_k < p.N;
-    const int64_t r = ok ? my_k : 0;
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) {
-      kf[kk] = frag_g(Kp + r * a.sk.n + 16 * kk + 8 * hh, ok);
-      if constexpr (!C::VLDS) vf[kk] = frag_g(Vp + r * a.sv.n + 16 * kk + 8 * hh, ok);
+  for (int rep = 0; rep < NREP; ++rep) {
+    const int kb = rep == 0 ? ui : nkb - 1 - ui;
+    if (rep == 1) {
+      if (kb == ui) break;  // the middle block of an odd count
+      __syncthreads();  // the first block's last step and V block are no longer read
     }
-  }
+    const int k0 = kb * C::BK;
+    const int my_k = k0 + 32 * w + lr;
+    const float sl2 = p.scale_l2;
+    const bool causal = p.causal != 0;
 
-  f32x16 dkt[C::NDB], dvt[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    dkt[db] = f32x16{};
-    dvt[db] = f32x16{};
-  }
+    const bf16* Kp = static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h;
+    const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
 
-  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
-  if (k0 < kvalid) {  // else every key of the block is masked: dK = dV = 0
-    // Steps run over (query head of the group) x (query block), limited to
-    // the rows that can see a key of this block: from the causal diagonal or
-    // the right window edge, up to the left window edge.
-    const int qfirst = max(p.causal ? k0 : 0, k0 - p.wr) / C::BQ;
-    const int qend = min(p.N, k0 + C::BK + p.wl);
-    const int nq = max(0, (qend + C::BQ - 1) / C::BQ - qfirst);
-    const int nsteps = p.G * nq;
-    auto next_step = [&](int st) {
-      while (st < nsteps && !block_on(p.bm, p.bm_ld, (qfirst + st % nq) * C::BQ, k0)) ++st;
-      return st;
-    };
-    const int qsb = 2 * (int)a.sq.n, dsb = 2 * (int)a.sdo.n;
-    int qvo[T::NLD], dvo[T::NLD];
-    if constexpr (!C::VLDS) {
-      dma_offsets<D, C::BQ>(qvo, qsb, w, lane);
-      dma_offsets<D, C::BQ>(dvo, dsb, w, lane);
-    }
-    static_assert(2 * C::NRC <= 4, "one wave per 64-row statistics load");
-    int roff_k[C::VLDS ? 1 : C::NKK], troff[C::NDB][2];
-    if constexpr (C::VLDS) {
-      // Only step 0's row offset stays live; the others are rebuilt per
-      // step (chunk 2 kk + hh of a swizzled row = step 0's offset XOR 32 kk).
-      roff_k[0] = T::off(swap_bits23(lr), hh);
-    } else {
-      row_offsets<D, C::BQ>(roff_k, lr, hh);
-    }
-    tr_offsets<D, C::BQ>(troff, lane);
-
-    // Q and dO tiles of a step and the LSE / D values of its rows all arrive
-    // by DMA into the stage; rows past the sequence read as zero, and with
-    // their Q and dO rows zero they add nothing to dK or dV.
-    auto issue = [&](int sidx, char* stage) {
-      const int h = hk * p.G + sidx / nq;
-      const int q0b = (qfirst + sidx % nq) * C::BQ;
-      const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
-                                 (uint32_t)(p.N - 1) * qsb + 2 * D);
-      const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
-                                 (uint32_t)(p.N - 1) * dsb + 2 * D);
-      // Registers are at their limit with the V block in LDS: rebuild the
-      // DMA offsets for this step from a lane index read afresh (an opaque
-      // mbcnt, so neither it nor the offsets are hoisted out of the loop and
-      // kept live, and nothing is reloaded from scratch, which would wait on
-      // the DMA just issued).
-      const int ln = C::VLDS ? fresh_lane_id() : lane;
-      if constexpr (C::VLDS) {
-        dma_offsets<D, C::BQ>(qvo, qsb, w, ln);
-        dma_offsets<D, C::BQ>(dvo, dsb, w, ln);
+    // This lane's key as the B operand of S = Q K^T and dP = dO V^T (V from
+    // LDS at d=128).
+    bf16x8 kf[C::NKK], vf[C::VLDS ? 1 : C::NKK];
+    {
+      const bool ok = my_k < p.N;
+      const int64_t r = ok ? my_k : 0;
+  #pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        kf[kk] = frag_g(Kp + r * a.sk.n + 16 * kk + 8 * hh, ok);
+        if constexpr (!C::VLDS) vf[kk] = frag_g(Vp + r * a.sv.n + 16 * kk + 8 * hh, ok);
       }
-      dma_tile<D, C::BQ>(qrs, qvo, (uint32_t)q0b * qsb, stage, w);
-      dma_tile<D, C::BQ>(drs, dvo, (uint32_t)q0b * dsb, stage + T::BYTES, w);
-      if (w < 2 * C::NRC) {  // wave-uniform: one 64-row load of LSE or D
-        const int64_t row0 = ((int64_t)b * p.Hq + h) * p.N;
-        const bool is_d = w >= C::NRC;
-        const int c = is_d ? w - C::NRC : w;
-        const Rsrc rs = make_rsrc((is_d ? a.dvec : a.lse2) + row0, (uint32_t)p.N * 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (FA_LDS void*)(stage + (is_d ? C::DVEC_OFF : C::LSE_OFF) + 256 * c), 4, 4 * ln,
-            (uint32_t)(q0b + 64 * c) * 4, 0, 0);
-      }
-    };
-
-    const int vb0 = C::VT::off(32 * w + lr, hh);
-    if constexpr (C::VLDS) {
-      using VT = typename C::VT;
-      static_assert((VT::RB & (VT::RB - 1)) == 0 && VT::CPR * 16 == VT::RB,
-                    "chunk field below a power-of-two row pitch");
-      int vvo[VT::NLD];
-      const int vsb = 2 * (int)a.sv.n;
-      dma_offsets<D, C::BK>(vvo, vsb, w, lane);
-      const Rsrc vrs = make_rsrc(Vp, (uint32_t)(p.N - 1) * vsb + 2 * D);
-      dma_tile<D, C::BK>(vrs, vvo, (uint32_t)k0 * vsb, smem + C::VOFF, w);
     }
 
-    int sidx = next_step(0);
-    if (sidx < nsteps) issue(sidx, smem);
-    wait_dma();  // the V block (if staged) and the first step
-    __syncthreads();
-    // One step reading stage `Qs` while the next lands in `fill`
-    // (restrict-qualified: these reads never wait for that DMA).
-    auto step = [&](const char* __restrict__ Qs, char* __restrict__ fill,
-                    const char* __restrict__ Vb) {
-      const char* dOs = Qs + T::BYTES;
-      const int h = hk * p.G + sidx / nq;
-      const int q0b = (qfirst + sidx % nq) * C::BQ;
-      // B-operand offsets of this lane's key row in the V block. The chunk
-      // field of a swizzled offset lies below the row pitch, so head-dim
-      // step kk (chunk 2 kk + hh) is step 0's offset XOR 32 kk; rebuilt each
-      // step from one live register (all eight kept live across the loop
-      // would push a row offset out to scratch).
-      int vboff[C::VLDS ? C::NKK : 1], roff[C::NKK];
-      if constexpr (C::VLDS) {
-        int v0 = vb0, r0 = roff_k[0];
-        asm volatile("" : "+v"(v0), "+v"(r0));
-#pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) {
-          vboff[kk] = v0 ^ (32 * kk);
-          roff[kk] = r0 ^ (32 * kk);
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk) roff[kk] = roff_k[kk];
-      }
-      const int nx = next_step(sidx + 1);
-      if (nx < nsteps) issue(nx, fill);  // lands during this step
-      // Dropout keep bits of this lane's key for every row of the step, made
-      // before the score products so that the generator's temporaries never
-      // share the registers with the S and dP accumulators (the empty asm
-      // with a memory clobber keeps the block ahead of the LDS reads). The 8
-      // lanes that share a key group (lane % 8 = key % 8) each run the
-      // generator for two rows of a sub-tile (perm_row(e, hh) and
-      // perm_row(8 + e, hh), e = lane % 8); a bit transpose across those
-      // lanes hands every lane bit r = row perm_row(r, hh).
-      uint32_t dbits[DROP ? C::NQS : 1];
-      if constexpr (DROP) {
-        const int ln = fresh_lane_id();
-        const int e = ln & 7, hl = ln >> 5;
-        const uint32_t kg = (uint32_t)(k0 + 32 * w + (ln & 24)) >> 3;
-        const uint32_t bh = (uint32_t)(b * p.Hq + h);
-#pragma unroll
-        for (int u = 0; u < C::NQS; ++u) {
-          const uint32_t row0 = (uint32_t)(q0b + 32 * u + 8 * hl + e);
-          const uint32_t lo = drop_byte(drop_bits(p, kg, row0, bh), p.drop_thr);
-          const uint32_t hi = drop_byte(drop_bits(p, kg, row0 + 16, bh), p.drop_thr);
-          dbits[u] = transpose8x8x2(lo | (hi << 8));
-          asm volatile("" : "+v"(dbits[u]) : : "memory");
-        }
-      }
-      if (a.log_kv && tid == 0)
-        log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
-      const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid) ||
-                             (q0b + C::BQ - 1 > k0 + p.wl) || (q0b < k0 + C::BK - 1 - p.wr);
+    f32x16 dkt[C::NDB], dvt[C::NDB];
+  #pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      dkt[db] = f32x16{};
+      dvt[db] = f32x16{};
+    }
 
-      // Straight-line step (no per-sub-tile branches): all S and dP products,
-      // one uniform mask block, then P / dS and the dV, dK products, so the
-      // compiler can overlap one sub-tile's exponentials with another's
-      // matrix products.
-      // FOLD: row statistics as chain starts. Lane half 0 reads LSE log2e /
-      // (scale log2e) of its A-operand row (clamped: an empty row's +inf
-      // becomes a finite value whose probabilities still underflow to 0),
-      // half 1 the row's D. S then starts at -LSE / scale and dP at -D
-      // (without dropout; with it dP starts at 0 and D is applied per
-      // element). Otherwise the 16 per-register values are read from LDS.
-      const float* stat_row = reinterpret_cast<const float*>(
-                                  Qs + ((lane >> 5) ? C::DVEC_OFF : C::LSE_OFF)) +
-                              swap_bits23(lr);
-      const float stat_mul = hh ? 1.f : 1.f / sl2;
-      auto row_stats = [&](int off, int u) {  // the 16 values of sub-tile u
-        const f32x4* v4 = reinterpret_cast<const f32x4*>(Qs + off) + 8 * u + 2 * hh;
-        return f32x4x4{v4[0], v4[1], v4[4], v4[5]};
+    const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
+    if (k0 < kvalid) {  // else every key of the block is masked: dK = dV = 0
+      // Steps run over (query head of the group) x (query block), limited to
+      // the rows that can see a key of this block: from the causal diagonal or
+      // the right window edge, up to the left window edge.
+      const int qfirst = max(p.causal ? k0 : 0, k0 - p.wr) / C::BQ;
+      const int qend = min(p.N, k0 + C::BK + p.wl);
+      const int nq = max(0, (qend + C::BQ - 1) / C::BQ - qfirst);
+      const int nsteps = p.G * nq;
+      auto next_step = [&](int st) {
+        while (st < nsteps && !block_on(p.bm, p.bm_ld, (qfirst + st % nq) * C::BQ, k0)) ++st;
+        return st;
       };
-#pragma unroll
-      for (int g0 = 0; g0 < C::NQS; g0 += C::NG) {
-        f32x16 s[C::NG], dp[C::NG];
-#pragma unroll
-        for (int uu = 0; uu < C::NG; ++uu) {
-          if constexpr (C::FOLD) {
-            const bf16x8 cf = split3_frag(fminf(stat_row[32 * (g0 + uu)] * stat_mul, 1e30f));
-            s[uu] = mfma(cf, neg_ones_frag(hh, 0), f32x16{});
-            dp[uu] = DROP ? f32x16{} : mfma(cf, neg_ones_frag(hh, 1), f32x16{});
-          } else {
-            s[uu] = f32x16{};
-            dp[uu] = f32x16{};
-          }
-          const char* qp = Qs + 32 * (g0 + uu) * T::RB;
-          const char* dop = dOs + 32 * (g0 + uu) * T::RB;
-#pragma unroll
-          for (int k4 = 0; k4 < C::NKK; k4 += C::FB) {
-            bf16x8 qa[C::FB], da[C::FB], va[C::FB];
-#pragma unroll
-            for (int i = 0; i < C::FB; ++i) {
-              qa[i] = lds_row(qp, roff[k4 + i]);
-              da[i] = lds_row(dop, roff[k4 + i]);
-              if constexpr (C::VLDS) va[i] = lds_row(Vb, vboff[k4 + i]);
-              else va[i] = vf[k4 + i];
-            }
-#pragma unroll
-            for (int i = 0; i < C::FB; ++i) {
-              s[uu] = mfma(qa[i], kf[k4 + i], s[uu]);
-              dp[uu] = mfma(da[i], va[i], dp[uu]);
-            }
-          }
-        }
-        // Register r of sub-tile u holds query row 32u + perm_row(r, hh).
-#pragma unroll
-        for (int uu = 0; uu < C::NG; ++uu) {
-          if constexpr (C::FOLD) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[uu][r] = __builtin_amdgcn_exp2f(s[uu][r] * sl2);
-          } else {
-            const f32x4x4 lv = row_stats(C::LSE_OFF, g0 + uu);
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              s[uu][r] = __builtin_amdgcn_exp2f(fmaf(s[uu][r], sl2, -lv.v[r >> 2][r & 3]));
-          }
-        }
-        if (__builtin_expect(need_mask, false)) {  // boundary tiles only
-          // Row qi sees key my_k iff qi - wl <= my_k <= qi + hi (hi = 0 under
-          // the causal mask, else the right window edge), i.e. iff
-          // qi - my_k + hi lies in [0, wl + hi]: one unsigned compare per
-          // element against a per-lane base (exact in 32-bit wrap-around for
-          // N <= 2^30).
-          // (The lane terms come from a fresh lane index: this rarely taken
-          // block would otherwise hold them live, or reload them from
-          // scratch, across the whole loop.)
-          const int ln = fresh_lane_id();
-          const int kl = k0 + 32 * w + (ln & 31);  // = my_k
-          const bool kpad = kl >= kvalid;
-          const unsigned hi = causal ? 0u : (unsigned)p.wr;
-          const unsigned span = (unsigned)p.wl + hi;
-          const unsigned base = (unsigned)(q0b + 8 * (ln >> 5)) + hi - (unsigned)kl;
-#pragma unroll
-          for (int uu = 0; uu < C::NG; ++uu)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const unsigned t = base + (unsigned)(32 * (g0 + uu) + perm_row(r, 0));
-              s[uu][r] = (kpad | (t > span)) ? 0.f : s[uu][r];  // branch-free select
-            }
-        }
-#pragma unroll
-        for (int uu = 0; uu < C::NG; ++uu) {
-          if constexpr (DROP) {
-            const f32x4x4 dv = row_stats(C::DVEC_OFF, g0 + uu);
-            const uint32_t bits = dbits[g0 + uu];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              // All-ones / all-zero mask from keep bit r; P o Z is one AND.
-              int m = __builtin_amdgcn_sbfe((int)bits, r, 1);
-              asm("" : "+v"(m));  // opaque: keeps the AND (not a compare + select)
-              const float pz = __int_as_float(__float_as_int(s[uu][r]) & m);
-              // dS' = P (Z dP~ - q D) = (P o Z) dP~ - P (q D)  (the D row
-              // vector holds q D); P o Z also feeds dV.
-              dp[uu][r] = fmaf(pz, dp[uu][r], -s[uu][r] * dv.v[r >> 2][r & 3]);
-              s[uu][r] = pz;
-            }
-          } else if constexpr (C::FOLD) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * dp[uu][r];  // dP started at -D
-          } else {
-            const f32x4x4 dv = row_stats(C::DVEC_OFF, g0 + uu);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * (dp[uu][r] - dv.v[r >> 2][r & 3]);
-          }
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const bf16x8 pf = pack8(s[uu], c);
-            const bf16x8 dsf = pack8(dp[uu], c);
-            const int rb = (32 * (g0 + uu) + 16 * c) * T::RB;
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-              dvt[db] = mfma(lds_tr(dOs + rb, troff[db][0], troff[db][1]), pf, dvt[db]);
-              dkt[db] = mfma(lds_tr(Qs + rb, troff[db][0], troff[db][1]), dsf, dkt[db]);
-            }
-          }
-        }
+      const int qsb = 2 * (int)a.sq.n, dsb = 2 * (int)a.sdo.n;
+      int qvo[T::NLD], dvo[T::NLD];
+      if constexpr (!C::VLDS) {
+        dma_offsets<D, C::BQ>(qvo, qsb, w, lane);
+        dma_offsets<D, C::BQ>(dvo, dsb, w, lane);
       }
-      if (nx < nsteps) {
-        wait_dma();
-        __syncthreads();
+      static_assert(2 * C::NRC <= 4, "one wave per 64-row statistics load");
+      int roff_k[C::VLDS ? 1 : C::NKK], troff[C::NDB][2];
+      if constexpr (C::VLDS) {
+        // Only step 0's row offset stays live; the others are rebuilt per
+        // step (chunk 2 kk + hh of a swizzled row = step 0's offset XOR 32 kk).
+        roff_k[0] = T::off(swap_bits23(lr), hh);
+      } else {
+        row_offsets<D, C::BQ>(roff_k, lr, hh);
       }
-      sidx = nx;
-    };
-    for (int st = 0; sidx < nsteps; st ^= 1)
-      step(smem + st * C::STAGE, smem + (st ^ 1) * C::STAGE, smem + C::VOFF);
-  }
+      tr_offsets<D, C::BQ>(troff, lane);
 
-  // Under dropout both products carry the 1 / q of the kept probabilities.
-  const float vscale = DROP ? p.drop_scale : 1.f;
-  const float kscale = p.scale * vscale;
-  if (my_k < p.N) {
-    bf16* dkp = static_cast<bf16*>(a.dk) + b * a.sdk.b + hk * a.sdk.h + (int64_t)my_k * a.sdk.n;
-    bf16* dvp = static_cast<bf16*>(a.dv) + b * a.sdv.b + hk * a.sdv.h + (int64_t)my_k * a.sdv.n;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * hh;
-        bf16x4 kq, vq;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kq[e] = (bf16)(dkt[db][4 * g + e] * kscale);
-          vq[e] = (bf16)(dvt[db][4 * g + e] * vscale);
+      // Q and dO tiles of a step and the LSE / D values of its rows all arrive
+      // by DMA into the stage; rows past the sequence read as zero, and with
+      // their Q and dO rows zero they add nothing to dK or dV.
+      auto issue = [&](int sidx, char* stage) {
+        const int h = hk * p.G + sidx / nq;
+        const int q0b = (qfirst + sidx % nq) * C::BQ;
+        const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
+                                   (uint32_t)(p.N - 1) * qsb + 2 * D);
+        const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
+                                   (uint32_t)(p.N - 1) * dsb + 2 * D);
+        // Registers are at their limit with the V block in LDS: rebuild the
+        // DMA offsets for this step from a lane index read afresh (an opaque
+        // mbcnt, so neither it nor the offsets are hoisted out of the loop and
+        // kept live, and nothing is reloaded from scratch, which would wait on
+        // the DMA just issued).
+        const int ln = C::VLDS ? fresh_lane_id() : lane;
+        if constexpr (C::VLDS) {
+          dma_offsets<D, C::BQ>(qvo, qsb, w, ln);
+          dma_offsets<D, C::BQ>(dvo, dsb, w, ln);
         }
-        *reinterpret_cast<bf16x4*>(dkp + d0) = kq;
-        *reinterpret_cast<bf16x4*>(dvp + d0) = vq;
+        dma_tile<D, C::BQ>(qrs, qvo, (uint32_t)q0b * qsb, stage, w);
+        dma_tile<D, C::BQ>(drs, dvo, (uint32_t)q0b * dsb, stage + T::BYTES, w);
+        if (w < 2 * C::NRC) {  // wave-uniform: one 64-row load of LSE or D
+          const int64_t row0 = ((int64_t)b * p.Hq + h) * p.N;
+          const bool is_d = w >= C::NRC;
+          const int c = is_d ? w - C::NRC : w;
+          const Rsrc rs = make_rsrc((is_d ? a.dvec : a.lse2) + row0, (uint32_t)p.N * 4);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (FA_LDS void*)(stage + (is_d ? C::DVEC_OFF : C::LSE_OFF) + 256 * c), 4, 4 * ln,
+              (uint32_t)(q0b + 64 * c) * 4, 0, 0);
+        }
+      };
+
+      const int vb0 = C::VT::off(32 * w + lr, hh);
+      if constexpr (C::VLDS) {
+        using VT = typename C::VT;
+        static_assert((VT::RB & (VT::RB - 1)) == 0 && VT::CPR * 16 == VT::RB,
+                      "chunk field below a power-of-two row pitch");
+        int vvo[VT::NLD];
+        const int vsb = 2 * (int)a.sv.n;
+        dma_offsets<D, C::BK>(vvo, vsb, w, lane);
+        const Rsrc vrs = make_rsrc(Vp, (uint32_t)(p.N - 1) * vsb + 2 * D);
+        dma_tile<D, C::BK>(vrs, vvo, (uint32_t)k0 * vsb, smem + C::VOFF, w);
       }
-  }
+
+      int sidx = next_step(0);
+      if (sidx < nsteps) issue(sidx, smem);
+      wait_dma();  // the V block (if staged) and the first step
+      __syncthreads();
+      // One step reading stage `Qs` while the next lands in `fill`
+      // (restrict-qualified: these reads never wait for that DMA).
+      auto step = [&](const char* __restrict__ Qs, char* __restrict__ fill,
+                      const char* __restrict__ Vb) {
+        const char* dOs = Qs + T::BYTES;
+        const int h = hk * p.G + sidx / nq;
+        const int q0b = (qfirst + sidx % nq) * C::BQ;
+        // B-operand offsets of this lane's key row in the V block. The chunk
+        // field of a swizzled offset lies below the row pitch, so head-dim
+        // step kk (chunk 2 kk + hh) is step 0's offset XOR 32 kk; rebuilt each
+        // step from one live register (all eight kept live across the loop
+        // would push a row offset out to scratch).
+        int vboff[C::VLDS ? C::NKK : 1], roff[C::NKK];
+        if constexpr (C::VLDS) {
+          int v0 = vb0, r0 = roff_k[0];
+          asm volatile("" : "+v"(v0), "+v"(r0));
+  #pragma unroll
+          for (int kk = 0; kk < C::NKK; ++kk) {
+            vboff[kk] = v0 ^ (32 * kk);
+            roff[kk] = r0 ^ (32 * kk);
+          }
+        } else {
+  #pragma unroll
+          for (int kk = 0; kk < C::NKK; ++kk) roff[kk] = roff_k[kk];
+        }
+        const int nx = next_step(sidx + 1);
+        if (nx < nsteps) issue(nx, fill);  // lands during this step
+        // Dropout keep bits of this lane's key for every row of the step, made
+        // before the score products so that the generator's temporaries never
+        // share the registers with the S and dP accumulators (the empty asm
+        // with a memory clobber keeps the block ahead of the LDS reads). The 8
+        // lanes that share a key group (lane % 8 = key % 8) each run the
+        // generator for two rows of a sub-tile (perm_row(e, hh) and
+        // perm_row(8 + e, hh), e = lane % 8); a bit transpose across those
+        // lanes hands every lane bit r = row perm_row(r, hh).
+        uint32_t dbits[DROP ? C::NQS : 1];
+        if constexpr (DROP) {
+          const int ln = fresh_lane_id();
+          const int e = ln & 7, hl = ln >> 5;
+          const uint32_t kg = (uint32_t)(k0 + 32 * w + (ln & 24)) >> 3;
+          const uint32_t bh = (uint32_t)(b * p.Hq + h);
+  #pragma unroll
+          for (int u = 0; u < C::NQS; ++u) {
+            const uint32_t row0 = (uint32_t)(q0b + 32 * u + 8 * hl + e);
+            const uint32_t lo = drop_byte(drop_bits(p, kg, row0, bh), p.drop_thr);
+            const uint32_t hi = drop_byte(drop_bits(p, kg, row0 + 16, bh), p.drop_thr);
+            dbits[u] = transpose8x8x2(lo | (hi << 8));
+            asm volatile("" : "+v"(dbits[u]) : : "memory");
+          }
+        }
+        if (a.log_kv && tid == 0)
+          log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
+        const bool need_mask = (p.causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid) ||
+                               (q0b + C::BQ - 1 > k0 + p.wl) || (q0b < k0 + C::BK - 1 - p.wr);
+
+        // Straight-line step (no per-sub-tile branches): all S and dP products,
+        // one uniform mask block, then P / dS and the dV, dK products, so the
+        // compiler can overlap one sub-tile's exponentials with another's
+        // matrix products.
+        // FOLD: row statistics as chain starts. Lane half 0 reads LSE log2e /
+        // (scale log2e) of its A-operand row (clamped: an empty row's +inf
+        // becomes a finite value whose probabilities still underflow to 0),
+        // half 1 the row's D. S then starts at -LSE / scale and dP at -D
+        // (without dropout; with it dP starts at 0 and D is applied per
+        // element). Otherwise the 16 per-register values are read from LDS.
+        const float* stat_row = reinterpret_cast<const float*>(
+                                    Qs + ((lane >> 5) ? C::DVEC_OFF : C::LSE_OFF)) +
+                                swap_bits23(lr);
+        const float stat_mul = hh ? 1.f : 1.f / sl2;
+        auto row_stats = [&](int off, int u) {  // the 16 values of sub-tile u
+          const f32x4* v4 = reinterpret_cast<const f32x4*>(Qs + off) + 8 * u + 2 * hh;
+          return f32x4x4{v4[0], v4[1], v4[4], v4[5]};
+        };
+  #pragma unroll
+        for (int g0 = 0; g0 < C::NQS; g0 += C::NG) {
+          f32x16 s[C::NG], dp[C::NG];
+  #pragma unroll
+          for (int uu = 0; uu < C::NG; ++uu) {
+            if constexpr (C::FOLD) {
+              const bf16x8 cf = split3_frag(fminf(stat_row[32 * (g0 + uu)] * stat_mul, 1e30f));
+              s[uu] = mfma(cf, neg_ones_frag(hh, 0), f32x16{});
+              dp[uu] = DROP ? f32x16{} : mfma(cf, neg_ones_frag(hh, 1), f32x16{});
+            } else {
+              s[uu] = f32x16{};
+              dp[uu] = f32x16{};
+            }
+            const char* qp = Qs + 32 * (g0 + uu) * T::RB;
+            const char* dop = dOs + 32 * (g0 + uu) * T::RB;
+  #pragma unroll
+            for (int k4 = 0; k4 < C::NKK; k4 += C::FB) {
+              bf16x8 qa[C::FB], da[C::FB], va[C::FB];
+  #pragma unroll
+              for (int i = 0; i < C::FB; ++i) {
+                qa[i] = lds_row(qp, roff[k4 + i]);
+                da[i] = lds_row(dop, roff[k4 + i]);
+                if constexpr (C::VLDS) va[i] = lds_row(Vb, vboff[k4 + i]);
+                else va[i] = vf[k4 + i];
+              }
+  #pragma unroll
+              for (int i = 0; i < C::FB; ++i) {
+                s[uu] = mfma(qa[i], kf[k4 + i], s[uu]);
+                dp[uu] = mfma(da[i], va[i], dp[uu]);
+              }
+            }
+          }
+          // Register r of sub-tile u holds query row 32u + perm_row(r, hh).
+  #pragma unroll
+          for (int uu = 0; uu < C::NG; ++uu) {
+            if constexpr (C::FOLD) {
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) s[uu][r] = __builtin_amdgcn_exp2f(s[uu][r] * sl2);
+            } else {
+              const f32x4x4 lv = row_stats(C::LSE_OFF, g0 + uu);
+  #pragma unroll
+              for (int r = 0; r < 16; ++r)
+                s[uu][r] = __builtin_amdgcn_exp2f(fmaf(s[uu][r], sl2, -lv.v[r >> 2][r & 3]));
+            }
+          }
+          if (__builtin_expect(need_mask, false)) {  // boundary tiles only
+            // Row qi sees key my_k iff qi - wl <= my_k <= qi + hi (hi = 0 under
+            // the causal mask, else the right window edge), i.e. iff
+            // qi - my_k + hi lies in [0, wl + hi]: one unsigned compare per
+            // element against a per-lane base (exact in 32-bit wrap-around for
+            // N <= 2^30).
+            // (The lane terms come from a fresh lane index: this rarely taken
+            // block would otherwise hold them live, or reload them from
+            // scratch, across the whole loop.)
+            const int ln = fresh_lane_id();
+            const int kl = k0 + 32 * w + (ln & 31);  // = my_k
+            const bool kpad = kl >= kvalid;
+            const unsigned hi = causal ? 0u : (unsigned)p.wr;
+            const unsigned span = (unsigned)p.wl + hi;
+            const unsigned base = (unsigned)(q0b + 8 * (ln >> 5)) + hi - (unsigned)kl;
+  #pragma unroll
+            for (int uu = 0; uu < C::NG; ++uu)
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const unsigned t = base + (unsigned)(32 * (g0 + uu) + perm_row(r, 0));
+                s[uu][r] = (kpad | (t > span)) ? 0.f : s[uu][r];  // branch-free select
+              }
+          }
+  #pragma unroll
+          for (int uu = 0; uu < C::NG; ++uu) {
+            if constexpr (DROP) {
+              const f32x4x4 dv = row_stats(C::DVEC_OFF, g0 + uu);
+              const uint32_t bits = dbits[g0 + uu];
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                // All-ones / all-zero mask from keep bit r; P o Z is one AND.
+                int m = __builtin_amdgcn_sbfe((int)bits, r, 1);
+                asm("" : "+v"(m));  // opaque: keeps the AND (not a compare + select)
+                const float pz = __int_as_float(__float_as_int(s[uu][r]) & m);
+                // dS' = P (Z dP~ - q D) = (P o Z) dP~ - P (q D)  (the D row
+                // vector holds q D); P o Z also feeds dV.
+                dp[uu][r] = fmaf(pz, dp[uu][r], -s[uu][r] * dv.v[r >> 2][r & 3]);
+                s[uu][r] = pz;
+              }
+            } else if constexpr (C::FOLD) {
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * dp[uu][r];  // dP started at -D
+            } else {
+              const f32x4x4 dv = row_stats(C::DVEC_OFF, g0 + uu);
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) dp[uu][r] = s[uu][r] * (dp[uu][r] - dv.v[r >> 2][r & 3]);
+            }
+  #pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const bf16x8 pf = pack8(s[uu], c);
+              const bf16x8 dsf = pack8(dp[uu], c);
+              const int rb = (32 * (g0 + uu) + 16 * c) * T::RB;
+  #pragma unroll
+              for (int db = 0; db < C::NDB; ++db) {
+                dvt[db] = mfma(lds_tr(dOs + rb, troff[db][0], troff[db][1]), pf, dvt[db]);
+                dkt[db] = mfma(lds_tr(Qs + rb, troff[db][0], troff[db][1]), dsf, dkt[db]);
+              }
+            }
+          }
+        }
+        if (nx < nsteps) {
+          wait_dma();
+          __syncthreads();
+        }
+        sidx = nx;
+      };
+      for (int st = 0; sidx < nsteps; st ^= 1)
+        step(smem + st * C::STAGE, smem + (st ^ 1) * C::STAGE, smem + C::VOFF);
+    }
+
+    // Under dropout both products carry the 1 / q of the kept probabilities.
+    const float vscale = DROP ? p.drop_scale : 1.f;
+    const float kscale = p.scale * vscale;
+    if (my_k < p.N) {
+      bf16* dkp = static_cast<bf16*>(a.dk) + b * a.sdk.b + hk * a.sdk.h + (int64_t)my_k * a.sdk.n;
+      bf16* dvp = static_cast<bf16*>(a.dv) + b * a.sdv.b + hk * a.sdv.h + (int64_t)my_k * a.sdv.n;
+  #pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * hh;
+          bf16x4 kq, vq;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kq[e] = (bf16)(dkt[db][4 * g + e] * kscale);
+            vq[e] = (bf16)(dvt[db][4 * g + e] * vscale);
+          }
+          *reinterpret_cast<bf16x4*>(dkp + d0) = kq;
+          *reinterpret_cast<bf16x4*>(dvp + d0) = vq;
+        }
+    }
+  }  // key blocks of this workgroup
 }
 
 // ----------------------------------------------------------------- dQ
@@ -671,15 +685,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // ----------------------------------------------------------------- launchers
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
-  const int64_t grid = (int64_t)((a.p.N + 127) / 128) * a.p.Hkv * a.p.B;
-  const dim3 g((unsigned)grid), blk(256);
+  const int64_t nkb = (a.p.N + 127) / 128;
+  const dim3 blk(256);
+  // Pairs of key blocks where the causal work shrinks with the block index.
+  const bool pair = a.p.causal && a.p.wl >= a.p.N;
+  const dim3 g((unsigned)((pair ? (nkb + 1) / 2 : nkb) * a.p.Hkv * a.p.B));
+#define FA_DKDV_LAUNCH(DD, DR)                                                           \
+  do {                                                                                   \
+    if (pair) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, DR, 2>), g, blk, 0, s, a);         \
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, DR, 1>), g, blk, 0, s, a);              \
+  } while (0)
   if (head_dim == 64) {
-    if (a.p.drop) hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), g, blk, 0, s, a);
+    if (a.p.drop) FA_DKDV_LAUNCH(64, true);
+    else FA_DKDV_LAUNCH(64, false);
   } else {
-    if (a.p.drop) hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), g, blk, 0, s, a);
+    if (a.p.drop) FA_DKDV_LAUNCH(128, true);
+    else FA_DKDV_LAUNCH(128, false);
   }
+#undef FA_DKDV_LAUNCH
   return hipGetLastError();
 }
 
