@@ -442,7 +442,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
       }
       kt = nxt;
     };
-    for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
+    // Unrolled by two so that each copy reads a stage at a fixed LDS address:
+    // every operand address is then a lane offset plus an immediate.
+    while (kt < ntiles) {
+      tile(smem[0], smem[1]);
+      if (kt >= ntiles) break;
+      tile(smem[1], smem[0]);
+    }
 
     const float l_tot = half_sum(l_run);
     const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;

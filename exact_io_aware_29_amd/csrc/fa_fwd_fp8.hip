@@ -277,7 +277,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_fp8(FwdArgs a) {
     }
     kt = nxt;
   };
-  for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
+  // Unrolled by two: each copy reads its stage at a fixed LDS address.
+  while (kt < ntiles) {
+    tile(smem[0], smem[1]);
+    if (kt >= ntiles) break;
+    tile(smem[1], smem[0]);
+  }
 
   const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? a.v_descale / l_tot : 0.f;
