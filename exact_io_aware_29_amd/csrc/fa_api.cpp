@@ -87,6 +87,19 @@ int check_tensor(const char* name, const void* ptr, fa_strides s, int dtype) {
   return FA_OK;
 }
 
+// The kernels address a head's rows of a staged tensor (K and V; Q and dO
+// in the backward) through a buffer resource with a 32-bit extent and 32-bit
+// byte offsets: the head's rows must span less than 4 GiB, and the row
+// stride must fit an int in bytes.
+int check_span(const char* name, fa_strides s, const fa_params* p, int dtype) {
+  const int64_t e = (int64_t)elem_size(dtype);
+  const int64_t span = (int64_t)(p->seqlen - 1) * s.row * e + (int64_t)p->head_dim * e;
+  if (s.row * e > INT32_MAX || span > (int64_t)UINT32_MAX)
+    return fail(FA_ERR_SHAPE, "%s: one head's rows span %lld bytes (row stride %lld); the limit is 4 GiB",
+                name, (long long)span, (long long)(s.row * e));
+  return FA_OK;
+}
+
 fa::Problem make_problem(const fa_params* p) {
   fa::Problem pr;
   pr.B = p->batch;
@@ -154,6 +167,8 @@ int fa_fwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   FA_CHECK(check_tensor("k", k, sk, p->dtype));
   FA_CHECK(check_tensor("v", v, sv, p->dtype));
   FA_CHECK(check_tensor("o", o, so, p->o_dtype));
+  FA_CHECK(check_span("k", sk, p, p->dtype));
+  FA_CHECK(check_span("v", sv, p, p->dtype));
   if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
   if (tile_log && reinterpret_cast<uintptr_t>(tile_log) % 4)
@@ -198,6 +213,10 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   FA_CHECK(check_tensor("dq", dq, sdq, p->dtype));
   FA_CHECK(check_tensor("dk", dk, sdk, p->dtype));
   FA_CHECK(check_tensor("dv", dv, sdv, p->dtype));
+  FA_CHECK(check_span("q", sq, p, p->dtype));
+  FA_CHECK(check_span("k", sk, p, p->dtype));
+  FA_CHECK(check_span("v", sv, p, p->dtype));
+  FA_CHECK(check_span("dout", sdo, p, p->dtype));
   if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
   const size_t need = fa_bwd_workspace_size(p);
@@ -303,6 +322,8 @@ int fa_decode(const fa_params* p, const void* q, fa_strides sq, const void* k, f
   FA_CHECK(check_tensor("k", k, sk, p->dtype));
   FA_CHECK(check_tensor("v", v, sv, p->dtype));
   FA_CHECK(check_tensor("o", o, so, p->o_dtype));
+  FA_CHECK(check_span("k", sk, p, p->dtype));
+  FA_CHECK(check_span("v", sv, p, p->dtype));
   if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
   const size_t need = fa_decode_workspace_size(p);

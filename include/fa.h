@@ -63,7 +63,11 @@ extern "C" {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,     /* a size is <= 0, or too large to index */
+  FA_ERR_SHAPE = -2,     /* a size is <= 0, or too large to index: this
+                          * includes one head's rows of K or V (and of Q or
+                          * dO in fa_bwd) spanning 4 GiB or more, that is
+                          * (seqlen - 1) * row stride + head_dim elements,
+                          * or a row stride of 2 GiB or more */
   FA_ERR_DTYPE = -3,     /* unsupported dtype combination */
   FA_ERR_HEADDIM = -4,   /* head_dim is not 64 or 128 */
   FA_ERR_GQA = -5,       /* heads_q is not a multiple of heads_kv */

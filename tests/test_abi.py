@@ -119,6 +119,32 @@ def test_fwd_rejects_bad_params(mut, code):
 
 
 @no_gpu_only
+def test_head_span_over_4_gib_is_rejected():
+    """Staged tensors are addressed per head through a 32-bit buffer extent:
+    (seqlen - 1) * row stride + head_dim elements must stay below 4 GiB."""
+    # contiguous d=128 rows: 2^24 + 1 rows of 256 bytes span just over 4 GiB
+    p = _params(batch=1, heads_q=1, heads_kv=1, seqlen=(1 << 24) + 1, head_dim=128)
+    st, detail = _fwd(p)
+    assert st == _abi.FA_ERR_SHAPE and "4 GiB" in detail, (st, detail)
+    # 2^24 - 1 rows stay inside: the span check passes (what follows needs a GPU)
+    p = _params(batch=1, heads_q=1, heads_kv=1, seqlen=(1 << 24) - 1, head_dim=128)
+    assert _fwd(p)[0] != _abi.FA_ERR_SHAPE
+    # a short sequence with a huge row stride
+    p = _params()
+    wide = _abi.Strides(0, 0, 1 << 26)
+    st, detail = _fwd(p, sk=wide)
+    assert st == _abi.FA_ERR_SHAPE and "k:" in detail, (st, detail)
+    # the backward also stages Q and dO
+    lib = fa.library()
+    s = _strides(p)
+    skv = _strides(p, p.heads_kv)
+    st = lib.fa_bwd(ctypes.byref(p), P16, wide, P32, skv, P48, skv, P64, s, P80, s,
+                    ctypes.c_void_p(0x6000), P16, s, P32, skv, P48, skv,
+                    ctypes.c_void_p(0x8000), 1 << 30, None, None, None)
+    assert st == _abi.FA_ERR_SHAPE, (st, lib.fa_last_error_detail().decode())
+
+
+@no_gpu_only
 def test_fwd_rejects_bad_pointers_and_strides():
     p = _params()
     assert _fwd(p, q=ctypes.c_void_p(0))[0] == _abi.FA_ERR_NULL
