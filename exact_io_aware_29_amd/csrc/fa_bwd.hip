@@ -556,6 +556,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       a.dvec[rowstat] = dq_d;
       a.lse2[rowstat] = lse2;
     }
+    // Without dropout every dP^T chain starts at -D (one value per lane: the
+    // lane's query row), set by one product from these two operands, so that
+    // dS = P dP needs no subtraction.
+    const bf16x8 d_split = split3_frag(dq_d), d_neg = neg_ones_frag(hh, 0);
 
     int kvo[T::NLD], vvo[T::NLD];
     dma_offsets<D, C::BC>(kvo, ksb, w, lane);
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
                              (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t) {
-        f32x16 st = f32x16{}, dpt = f32x16{};
+        f32x16 st = f32x16{}, dpt = DROP ? f32x16{} : mfma(d_neg, d_split, f32x16{});
         const char* kp = Ks + 32 * t * T::RB;
         const char* vp = Vs + 32 * t * T::RB;
         // Raised priority while this wave feeds the matrix pipe, so that the
@@ -646,7 +650,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
                       p.drop_thr);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (dpt[r] - dq_d);
+        for (int r = 0; r < 16; ++r) dpt[r] = st[r] * (DROP ? dpt[r] - dq_d : dpt[r]);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
