@@ -42,6 +42,10 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write this many MiB of scratch between timed steps (outside the "
+                         "kernel events) so that no K/V tile survives in L2 or MALL from one "
+                         "step to the next; value then comes from the summed kernel times")
     ap.add_argument("--workload", type=int, default=2,
                     help="workload id (2 = the headline B64 H16 N1024 d64 shape; 7 = decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -270,8 +274,13 @@ def device_info():
     """Name, compute units and architecture of the GPU the numbers come from."""
     import torch
     pr = torch.cuda.get_device_properties(0)
-    return {"name": pr.name, "compute_units": pr.multi_processor_count,
-            "arch": getattr(pr, "gcnArchName", "")}
+    rec = {"name": pr.name, "compute_units": pr.multi_processor_count,
+           "arch": getattr(pr, "gcnArchName", ""),
+           "peak_clock_assumed_mhz": 2400}
+    clk = getattr(pr, "clock_rate", None)  # kHz, where torch exposes it
+    if clk:
+        rec["max_clock_mhz"] = round(clk / 1000)
+    return rec
 
 
 def cpu_model():
@@ -421,8 +430,12 @@ def main():
             e.record()  # create the events outside the timed region
     torch.cuda.synchronize()
 
+    scratch = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
+               if args.flush_mib else None)
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(float(i))  # evicts L2 and MALL between steps
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -444,6 +457,8 @@ def main():
     pairs = sum(per_b) * w.heads_q
     fl = acc.flops(pairs, w.head_dim)
     ms_step = wall / args.steps * 1e3
+    if scratch is not None:  # the scratch writes are not part of a step
+        ms_step = sum(kern_ms.values())
     step_flop = fl["fwd_bwd"] if w.backward else fl["fwd"]
     value = step_flop / (ms_step * 1e-3) / 1e12
     peak = {"bf16": acc.MFMA_BF16_PEAK_TFLOPS, "fp8": acc.MFMA_FP8_PEAK_TFLOPS}.get(
@@ -496,6 +511,9 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if scratch is not None:
+        rec["flush_mib"] = args.flush_mib
+        rec["timing"] = "sum of kernel event times; scratch written between steps"
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, per_b, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
