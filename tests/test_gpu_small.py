@@ -155,6 +155,38 @@ def _check_fp32(case, window):
                           expected_tiles(B, Hq, N, causal, inp.seqlens, inp.block_mask, window))
 
 
+ISOLATED_BWD_CASES = [
+    (2, 4, 2, 300, 64, False, "random", None),
+    (3, 2, 2, 257, 64, True, [0, 1, 200], None),
+    (1, 2, 1, 520, 128, True, None, "random"),
+    (2, 4, 4, 384, 128, True, [384, 130], "butterfly"),
+]
+
+
+@pytest.mark.parametrize("case", ISOLATED_BWD_CASES, ids=_ids)
+def test_backward_on_the_oracle_forward(case):
+    """The backward alone: fed the oracle's O (fp32) and LSE instead of the
+    GPU forward's, so its error is measured apart from the forward's. Empty
+    rows arrive with LSE = -inf, as the forward would store them."""
+    B, Hq, Hkv, N, d, causal, sl, bm = case
+    inp = draw_case(B, Hq, Hkv, N, d, "bf16", causal=causal, seqlens=sl, block_mask=bm,
+                    seed=7 * N + d)
+    print(f"isolated backward {_ids(case)}", flush=True)
+    o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = _oracle_full(inp)
+    q, k, v = dev(inp.q, "bf16"), dev(inp.k, "bf16"), dev(inp.v, "bf16")
+    do = dev(inp.do, "bf16")
+    o = torch.from_numpy(o_ref.astype(np.float32)).cuda()
+    lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
+    slt = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).cuda()
+    bmt = None if inp.block_mask is None else torch.from_numpy(inp.block_mask).cuda()
+    dq, dk, dv, _ = fa.fa_bwd(q, k, v, o, lse, do, scale=inp.scale, causal=causal,
+                              seqlens_k=slt, block_mask=bmt)
+    torch.cuda.synchronize()
+    for name, g, ref in (("dQ", dq, dq_ref), ("dK", dk, dk_ref), ("dV", dv, dv_ref)):
+        r = check_grad(host64(g), ref, name, _ids(case))
+        print(f"  {name} relF {r:.2e}", flush=True)
+
+
 def test_strided_bshd_layout():
     """[B, N, H, d] storage viewed as [B, H, N, d]: strides, not copies."""
     B, H, N, d = 2, 3, 200, 64
