@@ -77,3 +77,36 @@ def test_decode_workload7_full_size():
                                                  seqlens=inp.seqlens[b:b + 1])
         check_o(host64(o[b:b + 1])[:, :, 0], o_ref, True, f"decode b{b}")
         check_lse(host64(lse[b:b + 1]), lse_ref, TOL_BF16_LSE, f"decode b{b}")
+
+
+def test_decode_cache_past_2_gib_per_head():
+    """A cache whose K (and V) rows of one head span 2.3 GB, past every 31-bit
+    byte offset and below the 4 GiB limit, with ragged lengths. Q = 0 makes
+    every allowed probability equal, so O is the mean of V over the cached
+    keys and LSE = ln(L): a closed form at any size (the mean is summed on
+    the GPU in fp64, in chunks)."""
+    B, Hq, Hkv, N, d = 2, 4, 1, 9_000_000, 128
+    lens = [N - 7, N // 2 + 3]
+    print(f"decode B{B} H{Hq}/{Hkv} N{N} d{d} lens {lens}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    k = torch.randn((B, Hkv, N, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, N, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    q = torch.zeros((B, Hq, 1, d), device="cuda", dtype=torch.bfloat16)
+    slt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o32, lse32 = fa.fa_decode(q, k, v, scale=d ** -0.5, seqlens_k=slt, o_dtype=torch.float32)
+    o, lse = fa.fa_decode(q, k, v, scale=d ** -0.5, seqlens_k=slt)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        acc = torch.zeros(d, dtype=torch.float64, device="cuda")
+        for r0 in range(0, L, 1 << 20):
+            acc += v[b, 0, r0:min(L, r0 + (1 << 20))].to(torch.float64).sum(dim=0)
+        mean = (acc / L).cpu().numpy()
+        for h in range(Hq):
+            err32 = np.abs(host64(o32[b, h, 0]) - mean).max()
+            assert err32 <= 2e-5, f"b{b} h{h} fp32 O err {err32:.3g}"
+            err = np.abs(host64(o[b, h, 0]) - mean)
+            assert (err <= 1e-5 + 2.0 ** -9 * np.abs(mean)).all(), f"b{b} h{h} bf16 O err {err.max():.3g}"
+            for name, l in (("fp32-O", lse32), ("bf16-O", lse)):
+                e = abs(float(l[b, h]) - np.log(L))
+                assert e <= 1e-5, f"b{b} h{h} {name} LSE err {e:.3g}"
+    del k, v
