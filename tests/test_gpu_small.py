@@ -211,6 +211,35 @@ def test_strided_bshd_layout():
     check_grad(host64(dv), dv_ref, "dV")
 
 
+def test_rows_spaced_past_2_gib():
+    """Q, K, V and dO rows 4 MiB apart: one head's 600 rows span 2.5 GB, so
+    every staged byte offset past row ~512 is beyond 2^31 (and below the
+    4 GiB limit). The strided views hold the same values as the dense case,
+    whose oracle is cheap."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 600, 64
+    S = (1 << 21) + 64  # row stride in elements (4 MiB + 128 bytes)
+    inp = draw_case(B, Hq, Hkv, N, d, "bf16", causal=True, seed=29)
+    print(f"rows {S * 2} bytes apart, span {((N - 1) * S + d) * 2} bytes per head", flush=True)
+    o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = _oracle_full(inp)
+
+    def spread(x, H):
+        big = torch.zeros(B * H * N * S, dtype=torch.bfloat16, device="cuda")
+        view = big.as_strided((B, H, N, d), (H * N * S, N * S, S, 1))
+        view.copy_(dev(x, "bf16"))
+        return view
+
+    q, k, v, do = spread(inp.q, Hq), spread(inp.k, Hkv), spread(inp.v, Hkv), spread(inp.do, Hq)
+    o, lse, _ = fa.fa_fwd(q, k, v, scale=inp.scale, causal=True)
+    dq, dk, dv, _ = fa.fa_bwd(q, k, v, o, lse, do, scale=inp.scale, causal=True)
+    torch.cuda.synchronize()
+    check_o(host64(o), o_ref, True)
+    check_lse(host64(lse), lse_ref, TOL_BF16_LSE)
+    check_grad(host64(dq), dq_ref, "dQ")
+    check_grad(host64(dk), dk_ref, "dK")
+    check_grad(host64(dv), dv_ref, "dV")
+    del q, k, v, do
+
+
 def test_deterministic_bitwise():
     inp = draw_case(2, 4, 2, 700, 128, "bf16", causal=True, seqlens="random", seed=5)
     (q, k, v, sl, bm), o1, l1, _ = _run(inp, tile_log=False)
