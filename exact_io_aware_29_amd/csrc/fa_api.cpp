@@ -74,6 +74,10 @@ int check_params(const fa_params* p) {
   if (p->block_mask && p->block_mask_ld < blocks)
     return fail(FA_ERR_MASK, "block_mask_ld %d < ceil(seqlen/128) = %lld", p->block_mask_ld,
                 (long long)blocks);
+  // The kernels read 64 consecutive blocks of a mask column at once, at
+  // 32-bit byte offsets of up to 63 pitches.
+  if (p->block_mask && p->block_mask_ld > (1 << 24))
+    return fail(FA_ERR_MASK, "block_mask_ld %d is above 2^24", p->block_mask_ld);
   return FA_OK;
 }
 

@@ -107,7 +107,11 @@ struct DkdvCfg {
   static_assert(STAGE % 256 == 0, "stages keep the 256-byte bank period");
 };
 
-template <int D, bool DROP, int NREP>
+// MASK: the block-mask scan is compiled in: for a launch with a mask, and
+// for every dropout launch, whose register allocation is better with it
+// (d=64 paired: no spill, against 2 without). Launches with neither leave
+// it out, which keeps their allocation as it was before the scan existed.
+template <int D, bool DROP, int NREP, bool MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<D>;
   using T = typename C::T;
@@ -176,9 +180,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       const int qend = min(p.N, k0 + C::BK + p.wl);
       const int nq = max(0, (qend + C::BQ - 1) / C::BQ - qfirst);
       const int nsteps = p.G * nq;
+      // Steps whose rows meet a present block of this key block's mask
+      // column; the column is the same for every query head of the group.
+      MaskLine mcol(MASK ? p.bm + (k0 >> 7) : nullptr, p.bm_ld, p.nlb);
       auto next_step = [&](int st) {
-        while (st < nsteps && !block_on(p.bm, p.bm_ld, (qfirst + st % nq) * C::BQ, k0)) ++st;
-        return st;
+        if constexpr (MASK) {
+          while (st < nsteps) {
+            const int g = st / nq, j = st - g * nq;
+            const int j2 = mcol.next_tile<C::BQ>(qfirst + j, qfirst + nq) - qfirst;
+            if (j2 < nq) return g * nq + j2;
+            st = (g + 1) * nq;  // none left in this head's rows: the next head
+          }
+          return nsteps;
+        } else {
+          return st;
+        }
       };
       const int qsb = 2 * (int)a.sq.n, dsb = 2 * (int)a.sdo.n;
       int qvo[T::NLD], dvo[T::NLD];
@@ -470,7 +486,8 @@ struct DqCfg {
   using T = SwzTile<D, BC>;
 };
 
-template <int D, bool DROP, int NREP>
+// MASK as in the dK/dV kernel.
+template <int D, bool DROP, int NREP, bool MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D>;
   using T = typename C::T;
@@ -577,9 +594,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const int ntiles = (kend + C::BC - 1) / C::BC;
     const int64_t log_row =
         a.log_q ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+    MaskLine mrow = mask_row(MASK ? p.bm : nullptr, p.bm_ld, p.nlb, q0);
+    // The tile index is wave-uniform; saying so keeps the DMA offsets in
+    // scalar registers (otherwise each buffer load may be wrapped in a
+    // read-first-lane loop).
     auto next_visit = [&](int kt) {
-      while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
-      return kt;
+      return __builtin_amdgcn_readfirstlane(MASK ? mrow.next_tile<C::BC>(kt, ntiles) : kt);
     };
     auto issue = [&](int kt, char* stage) {
       dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
@@ -694,10 +714,16 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   // Pairs of key blocks where the causal work shrinks with the block index.
   const bool pair = a.p.causal && a.p.wl >= a.p.N;
   const dim3 g((unsigned)((pair ? (nkb + 1) / 2 : nkb) * a.p.Hkv * a.p.B));
+  const bool mask = a.p.bm != nullptr || a.p.drop;
 #define FA_DKDV_LAUNCH(DD, DR)                                                           \
   do {                                                                                   \
-    if (pair) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, DR, 2>), g, blk, 0, s, a);         \
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, DR, 1>), g, blk, 0, s, a);              \
+    if (pair) {                                                                          \
+      if (mask) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, DR, 2, true>), g, blk, 0, s, a); \
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, DR, 2, DR>), g, blk, 0, s, a);     \
+    } else {                                                                             \
+      if (mask) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, DR, 1, true>), g, blk, 0, s, a); \
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<DD, DR, 1, DR>), g, blk, 0, s, a);     \
+    }                                                                                    \
   } while (0)
   if (head_dim == 64) {
     if (a.p.drop) FA_DKDV_LAUNCH(64, true);
@@ -716,10 +742,16 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
   // Pairs of query blocks where the causal work grows with the block index.
   const bool pair = a.p.causal && a.p.wl >= a.p.N;
   const dim3 g((unsigned)(pair ? ((a.p.N + 127) / 128 + 1) / 2 * a.p.Hq * a.p.B : grid));
+  const bool mask = a.p.bm != nullptr || a.p.drop;
 #define FA_DQ_LAUNCH(DD, DR)                                                             \
   do {                                                                                   \
-    if (pair) hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 2>), g, blk, 0, s, a);           \
-    else hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 1>), g, blk, 0, s, a);                \
+    if (pair) {                                                                          \
+      if (mask) hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 2, true>), g, blk, 0, s, a);   \
+      else hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 2, DR>), g, blk, 0, s, a);       \
+    } else {                                                                             \
+      if (mask) hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 1, true>), g, blk, 0, s, a);   \
+      else hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 1, DR>), g, blk, 0, s, a);       \
+    }                                                                                    \
   } while (0)
   if (head_dim == 64) {
     if (a.p.drop) FA_DQ_LAUNCH(64, true);

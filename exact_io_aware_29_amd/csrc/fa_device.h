@@ -137,9 +137,62 @@ __device__ __forceinline__ int valid_keys(const int32_t* seqlens, int b, int n) 
   return L < 0 ? 0 : (L > n ? n : L);
 }
 
-// Whether the 128 x 128 block (query row qrow, key col kcol) is present.
-__device__ __forceinline__ bool block_on(const uint8_t* bm, int ld, int qrow, int kcol) {
-  return bm == nullptr || bm[(int64_t)(qrow >> 7) * ld + (kcol >> 7)] != 0;
+// Present 128 x 128 blocks along one line (a row or a column) of a block
+// mask, looked up 64 blocks at a time: lane l tests block base + l, and one
+// wave ballot gathers the 64 answers, which stay cached for the following
+// lookups. A run of absent blocks then costs one vector load per 64 blocks
+// instead of one dependent load per tile (at N = 65536 a sparse row would
+// otherwise take about a thousand serial loads to find its ten blocks).
+// Every call is made by a full wave with wave-uniform arguments, so the
+// window lives in scalar registers.
+struct MaskLine {
+  const uint8_t* p;  // the line's first block; null when there is no mask
+  int64_t step;      // bytes from one block of the line to the next
+  int n;             // blocks on the line
+  int base;          // first block of the cached window
+  uint64_t bits;     // bit i: block base + i is present
+
+  __device__ __forceinline__ MaskLine(const uint8_t* first, int64_t stride, int nblocks)
+      : p(first), step(stride), n(nblocks), base(-64), bits(0) {}
+
+  // First present block at or after blk, or n if none is; blk itself when
+  // there is no mask.
+  __device__ __forceinline__ int next(int blk) {
+    if (p == nullptr) return blk;
+    while (blk < n) {
+      if (blk < base || blk >= base + 64) {
+        // A scalar window address plus a 32-bit lane offset (lane * step <
+        // 2^31: the block-mask pitch is limited to 2^24 bytes), with the lane
+        // index made on the spot, so the reload holds few vector registers.
+        base = blk;
+        const uint8_t* w = p + (int64_t)base * step;
+        int ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const bool on = base + ln < n && w[(uint32_t)ln * (uint32_t)step] != 0;
+        bits = __builtin_amdgcn_ballot_w64(on);
+      }
+      const uint64_t m = bits >> (blk - base);
+      if (m != 0) return blk + __builtin_ctzll(m);
+      blk = base + 64;
+    }
+    return n;
+  }
+
+  // First tile index >= t (tiles of BC keys or rows along the line) whose
+  // block is present, or a value >= tend if none is before tend.
+  template <int BC>
+  __device__ __forceinline__ int next_tile(int t, int tend) {
+    static_assert(BC <= 128 && 128 % BC == 0, "tiles subdivide a mask block");
+    if (t >= tend) return t;
+    const int b0 = (t * BC) >> 7;
+    const int blk = next(b0);
+    return blk == b0 ? t : min(tend, blk * (128 / BC));
+  }
+};
+
+// Mask row of the query block starting at row q0 (a multiple of 128).
+__device__ __forceinline__ MaskLine mask_row(const uint8_t* bm, int ld, int nlb, int q0) {
+  return MaskLine(bm ? bm + (int64_t)(q0 >> 7) * ld : nullptr, 1, nlb);
 }
 
 __device__ __forceinline__ void log_tile(uint32_t* log, int64_t row_word0, int kcol) {

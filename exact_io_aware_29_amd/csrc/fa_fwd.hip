@@ -93,9 +93,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const int64_t log_row =
       a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
 
-  for (int kt = max(0, q0 - p.wl) / C::BC; kt < ntiles; ++kt) {
+  // Visited tiles only: the block-mask scan is uniform per workgroup.
+  MaskLine mrow = mask_row(p.bm, p.bm_ld, p.nlb, q0);
+  for (int kt = mrow.next_tile<C::BC>(max(0, q0 - p.wl) / C::BC, ntiles); kt < ntiles;
+       kt = mrow.next_tile<C::BC>(kt + 1, ntiles)) {
     const int key0 = kt * C::BC;
-    if (!block_on(p.bm, p.bm_ld, q0, key0)) continue;  // uniform per workgroup
     __syncthreads();
     stage_rows<T, D, C::BC, C::KROW>(Kp, a.sk.n, key0, p.N, Ks, tid);
     stage_cols<T, D, C::BC, C::VROW>(Vp, a.sv.n, key0, p.N, Vt, tid);
@@ -242,7 +244,11 @@ struct FwdB {
   static constexpr float kLag = 8.f;
 };
 
-template <int D, bool DROP, int NREP>
+// MASK: the block-mask scan is compiled in. A launch with a mask needs it;
+// one without a mask and without dropout leaves it out. Dropout launches
+// keep it either way: their register allocation is better with it (d=64:
+// 128 VGPRs, four waves per SIMD, against 149 without).
+template <int D, bool DROP, int NREP, bool MASK>
 __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   using C = FwdB<D>;
   using T = typename C::T;
@@ -312,10 +318,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
     const int64_t log_row =
         a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
 
-    auto next_visit = [&](int kt) {
-      while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
-      return kt;
-    };
+    MaskLine mrow = mask_row(MASK ? p.bm : nullptr, p.bm_ld, p.nlb, q0);
+    auto next_visit = [&](int kt) { return MASK ? mrow.next_tile<C::BC>(kt, ntiles) : kt; };
     auto issue = [&](int kt, char* stage) {
       dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
       dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
@@ -490,21 +494,26 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool DROP, int NREP>
+static void launch_fwd_bf16_m(const FwdArgs& a, dim3 g, hipStream_t s) {
+  if (DROP || a.p.bm) hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, true>), g, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, DROP>), g, dim3(256), 0, s, a);
+}
+
 template <int D>
 static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const int64_t nqb = (a.p.N + FwdB<D>::BR - 1) / FwdB<D>::BR;
-  const dim3 blk(256);
   // Pairs of query blocks where the work per block grows with the block
   // index (causal, no left window edge); under a sliding window every block
   // already does about the same work.
   if (a.p.causal && a.p.wl >= a.p.N) {
     const dim3 g((unsigned)(((nqb + 1) / 2) * a.p.Hq * a.p.B));
-    if (a.p.drop) hipLaunchKernelGGL((fwd_kernel_bf16<D, true, 2>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel_bf16<D, false, 2>), g, blk, 0, s, a);
+    if (a.p.drop) launch_fwd_bf16_m<D, true, 2>(a, g, s);
+    else launch_fwd_bf16_m<D, false, 2>(a, g, s);
   } else {
     const dim3 g((unsigned)(nqb * a.p.Hq * a.p.B));
-    if (a.p.drop) hipLaunchKernelGGL((fwd_kernel_bf16<D, true, 1>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel_bf16<D, false, 1>), g, blk, 0, s, a);
+    if (a.p.drop) launch_fwd_bf16_m<D, true, 1>(a, g, s);
+    else launch_fwd_bf16_m<D, false, 1>(a, g, s);
   }
   return hipGetLastError();
 }

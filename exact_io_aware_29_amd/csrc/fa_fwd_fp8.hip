@@ -170,10 +170,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_fp8(FwdArgs a) {
   const int64_t log_row =
       a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
 
-  auto next_visit = [&](int kt) {
-    while (kt < ntiles && !block_on(p.bm, p.bm_ld, q0, kt * C::BC)) ++kt;
-    return kt;
-  };
+  MaskLine mrow = mask_row(p.bm, p.bm_ld, p.nlb, q0);
+  auto next_visit = [&](int kt) { return mrow.next_tile<C::BC>(kt, ntiles); };
   auto issue = [&](int kt, char* stage) {
     dma_tile8<T>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
     dma_tile8<T>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);

@@ -75,7 +75,7 @@ enum fa_status {
   FA_ERR_ALIGN = -7,     /* a base pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = -8, /* workspace missing or smaller than required */
   FA_ERR_HIP = -9,       /* a HIP call failed (see fa_last_error_detail) */
-  FA_ERR_MASK = -10,     /* block_mask_ld smaller than ceil(seqlen / 128) */
+  FA_ERR_MASK = -10,     /* block_mask_ld below ceil(seqlen / 128) or above 2^24 */
   FA_ERR_SCALE = -11,    /* scale is not finite and positive */
   FA_ERR_DROPOUT = -12   /* dropout_p outside [0, 1) or too close to 1 */
 };
@@ -116,7 +116,7 @@ typedef struct fa_params {
   const int32_t* seqlens_k;  /* device [batch] valid key counts, or NULL;
                                 values are clamped to [0, seqlen] */
   const uint8_t* block_mask; /* device [ceil(N/128)][block_mask_ld], or NULL */
-  int32_t block_mask_ld;     /* row pitch of block_mask in bytes */
+  int32_t block_mask_ld;     /* row pitch of block_mask in bytes, at most 2^24 */
   /* Sliding-window (local) attention, ANDed with the masks above: when
    * `window` is nonzero, key j is allowed for query i only if
    * i - window_left <= j <= i + window_right (both >= 0; FA_ERR_MASK

@@ -98,6 +98,7 @@ def _fwd(p, q=P16, k=P32, v=P48, o=P64, lse=P80, sq=None, sk=None, so=None, log=
     (dict(dtype=7), _abi.FA_ERR_DTYPE),
     (dict(dtype=_abi.FA_FP32, o_dtype=_abi.FA_BF16), _abi.FA_ERR_DTYPE),
     (dict(block_mask=0x9000, block_mask_ld=2), _abi.FA_ERR_MASK),
+    (dict(block_mask=0x9000, block_mask_ld=(1 << 24) + 16), _abi.FA_ERR_MASK),
     (dict(window=(-1, 4)), _abi.FA_ERR_MASK),
     (dict(window=(3, -2)), _abi.FA_ERR_MASK),
     (dict(dropout_p=1.0), _abi.FA_ERR_DROPOUT),
