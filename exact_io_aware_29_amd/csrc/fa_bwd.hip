@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       // column; the column is the same for every query head of the group.
       MaskLine mcol(MASK ? p.bm + (k0 >> 7) : nullptr, p.bm_ld, p.nlb);
       auto next_step = [&](int st) {
-        if constexpr (MASK) {
+        if (MASK && p.bm != nullptr) {
           while (st < nsteps) {
             const int g = st / nq, j = st - g * nq;
             const int j2 = mcol.next_tile<C::BQ>(qfirst + j, qfirst + nq) - qfirst;
@@ -194,6 +194,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
           return nsteps;
         } else {
           return st;
+        }
+      };
+      // Step sidx -> (query head, first row). Without a mask: query blocks
+      // from the last one down, heads of the group innermost, so that the
+      // workgroups of one key/value head start on the same Q and dO tiles
+      // and share them through L2. With a mask: heads outer, blocks upward
+      // (the order of the mask scan).
+      auto step_unit = [&](int sidx, int& h, int& q0b) {
+        if (MASK && p.bm != nullptr) {
+          h = hk * p.G + sidx / nq;
+          q0b = (qfirst + sidx % nq) * C::BQ;
+        } else {
+          const int jd = p.G == 1 ? sidx : sidx / p.G;
+          h = hk * p.G + (sidx - jd * p.G);
+          q0b = (qfirst + nq - 1 - jd) * C::BQ;
         }
       };
       const int qsb = 2 * (int)a.sq.n, dsb = 2 * (int)a.sdo.n;
@@ -217,8 +232,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       // by DMA into the stage; rows past the sequence read as zero, and with
       // their Q and dO rows zero they add nothing to dK or dV.
       auto issue = [&](int sidx, char* stage) {
-        const int h = hk * p.G + sidx / nq;
-        const int q0b = (qfirst + sidx % nq) * C::BQ;
+        int h, q0b;
+        step_unit(sidx, h, q0b);
         const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
                                    (uint32_t)(p.N - 1) * qsb + 2 * D);
         const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
@@ -267,8 +282,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       auto step = [&](const char* __restrict__ Qs, char* __restrict__ fill,
                       const char* __restrict__ Vb) {
         const char* dOs = Qs + T::BYTES;
-        const int h = hk * p.G + sidx / nq;
-        const int q0b = (qfirst + sidx % nq) * C::BQ;
+        int h, q0b;
+        step_unit(sidx, h, q0b);
         // B-operand offsets of this lane's key row in the V block. The chunk
         // field of a swizzled offset lies below the row pitch, so head-dim
         // step kk (chunk 2 kk + hh) is step 0's offset XOR 32 kk; rebuilt each
