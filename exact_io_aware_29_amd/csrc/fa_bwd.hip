@@ -637,8 +637,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
       const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
                              (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
+      // Causal pairs: a wave whose 32 rows lie above every key of a 32-key
+      // sub-tile skips it (its P would be 0 and so would its dS, leaving dQ
+      // bit-identical). One-block launches compile no test.
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t) {
+        if (NREP == 2 && key0 + 32 * t > q0 + 32 * w + 31) continue;
         f32x16 st = f32x16{}, dpt = DROP ? f32x16{} : mfma(d_neg, d_split, f32x16{});
         const char* kp = Ks + 32 * t * T::RB;
         const char* vp = Vs + 32 * t * T::RB;

@@ -344,6 +344,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
       const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
                              (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
 
+      // Causal pairs: a wave whose 32 rows lie above every key of the tile
+      // skips it (every score would be -inf, every P~ exactly 0, and m, l and
+      // O would come out bit-identical). One-block launches compile no test,
+      // which keeps their register allocation.
+      const bool wave_off = NREP == 2 && key0 > q0 + 32 * w + 31;
+      if (!wave_off) {
       // One straight-line block per tile (no per-sub-tile branches), so the
       // compiler can overlap one sub-tile's exponentials with its neighbour's
       // matrix products: all S^T products, one max and lazy-rescale test for
@@ -440,6 +446,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
         }
         __builtin_amdgcn_s_setprio(0);
       }
+      }  // !wave_off
       if (nxt < ntiles) {
         wait_dma();
         __syncthreads();  // next tile landed everywhere; this tile is no longer read
