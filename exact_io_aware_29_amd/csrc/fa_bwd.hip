@@ -352,6 +352,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         };
   #pragma unroll
         for (int g0 = 0; g0 < C::NQS; g0 += C::NG) {
+          // Causal pairs at d=128: when every row of the step lies above all
+          // 32 keys of this wave, the wave's P is exactly 0 and the step adds
+          // nothing to dK or dV; it is skipped (6 of the 16 wave-steps of the
+          // diagonal block). One-block launches and d=64, whose paired
+          // dropout kernel would spill with it, compile no test.
+          if (D == 128 && NREP == 2 && q0b + 32 * (g0 + C::NG) - 1 < k0 + 32 * w) continue;
           f32x16 s[C::NG], dp[C::NG];
   #pragma unroll
           for (int uu = 0; uu < C::NG; ++uu) {
