@@ -88,3 +88,22 @@ def test_mask_scan_across_windows(d, causal):
     kv = ref[(0, 0, "kv")]
     check_grad(host64(dk[0, 0])[k_rows], kv["dk"], "dK")
     check_grad(host64(dv[0, 0])[k_rows], kv["dv"], "dV")
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
+def test_fp8_forward_mask_scan_across_windows(d, causal):
+    """The FP8 forward walks the same mask rows: its visited tiles must equal
+    the mask exactly, and rows of the empty mask row must give O = 0 and
+    LSE = -inf (values of visited rows are covered by the FP8 parity tests)."""
+    print(f"fp8 mask scan N{N} d{d} causal={causal}", flush=True)
+    bm = mask()
+    g = torch.Generator(device="cpu").manual_seed(d)
+    q, k, v = (torch.randn((1, 2 if i == 0 else 1, N, d), generator=g).to(torch.float8_e4m3fn)
+               .cuda() for i in range(3))
+    o, lse, flog = fa.fa_fwd(q, k, v, causal=causal, block_mask=torch.from_numpy(bm).cuda(),
+                             tile_log=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(decode_log(flog, 1, 2, N), expected_tiles(1, 2, N, causal, None, bm))
+    r = slice(EMPTY_ROW * 128, EMPTY_ROW * 128 + 128)
+    assert torch.all(o[0, :, r].float() == 0) and torch.all(torch.isneginf(lse[0, :, r]))
+    assert torch.isfinite(o.float()).all()
