@@ -125,7 +125,7 @@ def cpu_baseline(inp, pairs_per_head, budget_s):
                 break
         el = time.perf_counter() - t0
         return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-                "kind": "oracle", "cpu": cpu_model(),
+                "kind": "oracle", "cpu": cpu_model(), "blas": blas_info(),
                 "sample": f"fp64 oracle forward{' and the dQ part of the backward' if w.backward else ''}"
                           f" over the first {rows_done} rows of (batch 0, head 0), {el:.1f} s; "
                           f"{'(4 + 6)' if w.backward else '4'} d flops per allowed pair"}
@@ -153,6 +153,7 @@ def cpu_baseline(inp, pairs_per_head, budget_s):
         "cores": int(cores),
         "kind": "oracle",
         "cpu": cpu_model(),
+        "blas": blas_info(),
         "sample": f"fp64 oracle {'fwd+bwd' if w.backward else 'fwd'} of the first {done} (batch, head) pairs of "
                   f"{w.batch * w.heads_q}, {el:.1f} s; same algorithmic flop count",
     }
@@ -182,7 +183,7 @@ def decode_cpu_baseline(inp, budget_s):
             break
     el = time.perf_counter() - t0
     return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle", "cpu": cpu_model(),
+            "kind": "oracle", "cpu": cpu_model(), "blas": blas_info(),
             "sample": f"fp64 oracle decode of the first {done} of {w.batch} sequences, "
                       f"{el:.1f} s; same algorithmic bytes"}
 
@@ -289,6 +290,20 @@ def cpu_model():
             if line.startswith("model name"):
                 return line.split(":", 1)[1].strip()
     except OSError:
+        pass
+    return "unknown"
+
+
+def blas_info():
+    """The BLAS numpy's oracle runs on, as threadpoolctl reports it."""
+    try:
+        import numpy  # noqa: F401  (loads the BLAS, so that it is listed)
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                arch = f" ({i['architecture']})" if i.get("architecture") else ""
+                return f"{i.get('internal_api', '?')} {i.get('version', '?')}{arch}"
+    except Exception:  # pragma: no cover
         pass
     return "unknown"
 

@@ -25,6 +25,7 @@ def _check_baseline(rec, unit):
     assert rec["kind"] == "oracle" and rec["unit"] == unit
     assert rec["value"] > 0 and rec["cores"] >= 1
     assert isinstance(rec["cpu"], str) and rec["sample"]
+    assert isinstance(rec["blas"], str) and rec["blas"]
 
 
 def test_cpu_baseline_fields_and_budget():
