@@ -107,10 +107,11 @@ struct DkdvCfg {
   static_assert(STAGE % 256 == 0, "stages keep the 256-byte bank period");
 };
 
-// MASK: the block-mask scan is compiled in: for a launch with a mask, and
-// for every dropout launch, whose register allocation is better with it
-// (d=64 paired: no spill, against 2 without). Launches with neither leave
-// it out, which keeps their allocation as it was before the scan existed.
+// MASK: the general variant, with the block-mask scan and (d=128) the
+// per-wave band skip compiled in, for launches with a block mask, a sliding
+// window or dropout (dropout launches allocate registers better with it: the
+// d=64 pair does not spill, against 2 spills without). Launches with none of
+// them use the lean variant, which keeps its register allocation.
 template <int D, bool DROP, int NREP, bool MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<D>;
@@ -352,12 +353,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         };
   #pragma unroll
         for (int g0 = 0; g0 < C::NQS; g0 += C::NG) {
-          // Causal pairs at d=128: when every row of the step lies above all
-          // 32 keys of this wave, the wave's P is exactly 0 and the step adds
-          // nothing to dK or dV; it is skipped (6 of the 16 wave-steps of the
-          // diagonal block). One-block launches and d=64, whose paired
-          // dropout kernel would spill with it, compile no test.
-          if (D == 128 && NREP == 2 && q0b + 32 * (g0 + C::NG) - 1 < k0 + 32 * w) continue;
+          // d=128: when no row of the step sees any of this wave's 32 keys
+          // (rows above the keys under the causal mask, or outside the band),
+          // the wave's P is exactly 0 and the step adds nothing to dK or dV;
+          // it is skipped (causal: 6 of the 16 wave-steps of the diagonal
+          // block). Causal pairs test the diagonal, one-block launches of the
+          // general variant without dropout the band; d=64, whose paired
+          // dropout kernel would spill with it, has no test.
+          if (D == 128 &&
+              (NREP == 2 ? q0b + 32 * (g0 + C::NG) - 1 < k0 + 32 * w
+                         : MASK && !DROP &&
+                               (q0b + 32 * (g0 + C::NG) - 1 + (causal ? 0 : p.wr) < k0 + 32 * w ||
+                                q0b + 32 * g0 - p.wl > k0 + 32 * w + 31)))
+            continue;
           f32x16 s[C::NG], dp[C::NG];
   #pragma unroll
           for (int uu = 0; uu < C::NG; ++uu) {
@@ -643,12 +651,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
       const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
                              (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
-      // Causal pairs: a wave whose 32 rows lie above every key of a 32-key
-      // sub-tile skips it (its P would be 0 and so would its dS, leaving dQ
-      // bit-identical). One-block launches compile no test.
+      // A wave whose 32 rows see no key of a 32-key sub-tile (above the
+      // causal diagonal, outside the band) skips it: its P would be 0 and so
+      // would its dS, leaving dQ bit-identical. Causal pairs test the
+      // diagonal, one-block launches of the general variant without dropout
+      // the band; the rest compile no test.
+      const int r0 = q0 + 32 * w;
 #pragma unroll
       for (int t = 0; t < C::NSUB; ++t) {
-        if (NREP == 2 && key0 + 32 * t > q0 + 32 * w + 31) continue;
+        if (NREP == 2 ? key0 + 32 * t > r0 + 31
+                      : MASK && !DROP && (key0 + 32 * t > r0 + 31 + (causal ? 0 : p.wr) ||
+                                          key0 + 32 * t + 31 < r0 - p.wl))
+          continue;
         f32x16 st = f32x16{}, dpt = DROP ? f32x16{} : mfma(d_neg, d_split, f32x16{});
         const char* kp = Ks + 32 * t * T::RB;
         const char* vp = Vs + 32 * t * T::RB;
@@ -739,7 +753,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   // Pairs of key blocks where the causal work shrinks with the block index.
   const bool pair = a.p.causal && a.p.wl >= a.p.N;
   const dim3 g((unsigned)((pair ? (nkb + 1) / 2 : nkb) * a.p.Hkv * a.p.B));
-  const bool mask = a.p.bm != nullptr || a.p.drop;
+  const bool mask = a.p.bm != nullptr || a.p.drop || a.p.wl < a.p.N || a.p.wr < a.p.N;
 #define FA_DKDV_LAUNCH(DD, DR)                                                           \
   do {                                                                                   \
     if (pair) {                                                                          \
@@ -767,7 +781,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
   // Pairs of query blocks where the causal work grows with the block index.
   const bool pair = a.p.causal && a.p.wl >= a.p.N;
   const dim3 g((unsigned)(pair ? ((a.p.N + 127) / 128 + 1) / 2 * a.p.Hq * a.p.B : grid));
-  const bool mask = a.p.bm != nullptr || a.p.drop;
+  const bool mask = a.p.bm != nullptr || a.p.drop || a.p.wl < a.p.N || a.p.wr < a.p.N;
 #define FA_DQ_LAUNCH(DD, DR)                                                             \
   do {                                                                                   \
     if (pair) {                                                                          \

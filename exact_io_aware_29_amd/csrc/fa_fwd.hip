@@ -244,10 +244,12 @@ struct FwdB {
   static constexpr float kLag = 8.f;
 };
 
-// MASK: the block-mask scan is compiled in. A launch with a mask needs it;
-// one without a mask and without dropout leaves it out. Dropout launches
-// keep it either way: their register allocation is better with it (d=64:
-// 128 VGPRs, four waves per SIMD, against 149 without).
+// MASK: the general variant, with the block-mask scan and the per-wave band
+// skip compiled in, for launches with a block mask, a sliding window or
+// dropout. Launches with none of them use the lean variant, which keeps its
+// register allocation. (Dropout launches take the general one even without a
+// mask: their allocation is better with it, 128 VGPRs and four waves per SIMD
+// at d=64 against 149 without.)
 template <int D, bool DROP, int NREP, bool MASK>
 __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   using C = FwdB<D>;
@@ -344,11 +346,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
       const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
                              (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);
 
-      // Causal pairs: a wave whose 32 rows lie above every key of the tile
-      // skips it (every score would be -inf, every P~ exactly 0, and m, l and
-      // O would come out bit-identical). One-block launches compile no test,
-      // which keeps their register allocation.
-      const bool wave_off = NREP == 2 && key0 > q0 + 32 * w + 31;
+      // A wave whose 32 rows see no key of the tile (above the causal
+      // diagonal, outside the band) skips it: every score would be -inf,
+      // every P~ exactly 0, and m, l and O come out bit-identical. Causal
+      // pairs test the diagonal; one-block launches of the general variant
+      // without dropout test the band; the rest compile no test.
+      const int r0 = q0 + 32 * w;
+      const bool wave_off =
+          NREP == 2 ? key0 > r0 + 31
+                    : MASK && !DROP &&
+                          (key0 > r0 + 31 + (p.causal ? 0 : p.wr) || key0 + C::BC - 1 < r0 - p.wl);
       if (!wave_off) {
       // One straight-line block per tile (no per-sub-tile branches), so the
       // compiler can overlap one sub-tile's exponentials with its neighbour's
@@ -503,7 +510,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
 
 template <int D, bool DROP, int NREP>
 static void launch_fwd_bf16_m(const FwdArgs& a, dim3 g, hipStream_t s) {
-  if (DROP || a.p.bm) hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, true>), g, dim3(256), 0, s, a);
+  if (DROP || a.p.bm || a.p.wl < a.p.N || a.p.wr < a.p.N)
+    hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, true>), g, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, DROP>), g, dim3(256), 0, s, a);
 }
 
