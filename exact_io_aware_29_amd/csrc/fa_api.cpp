@@ -14,6 +14,12 @@
 #include "../../include/fa.h"
 #include "fa_internal.h"
 
+#define FA_CHECK(expr)            \
+  do {                            \
+    const int st_ = (expr);       \
+    if (st_ != FA_OK) return st_; \
+  } while (0)
+
 namespace {
 
 thread_local char g_detail[256] = "";
@@ -91,16 +97,36 @@ int check_tensor(const char* name, const void* ptr, fa_strides s, int dtype) {
   return FA_OK;
 }
 
+// Rows of one head must not overlap: the kernels read a tile's rows past
+// the sequence (or past a batch entry's valid key count) as zeros through a
+// buffer resource whose extent ends at the last valid row, which only
+// excludes the rows after it if each row starts past the previous row's
+// data. Outputs with overlapping rows would be written by several lanes.
+int check_rows(const char* name, fa_strides s, const fa_params* p) {
+  if (s.row < p->head_dim)
+    return fail(FA_ERR_STRIDE, "%s: row stride %lld is below head_dim %d (rows overlap)", name,
+                (long long)s.row, p->head_dim);
+  return FA_OK;
+}
+
 // The kernels address a head's rows of a staged tensor (K and V; Q and dO
-// in the backward) through a buffer resource with a 32-bit extent and 32-bit
-// byte offsets: the head's rows must span less than 4 GiB, and the row
-// stride must fit an int in bytes.
+// in the backward) through a buffer resource with 32-bit byte offsets and a
+// 32-bit extent. Tiles cover whole 128-row blocks, so the rows addressed run
+// up to ceil(N / 128) * 128 - 1, past the last row when N is not a multiple
+// of 128: every byte of every such row must lie below offset 2^32, or its
+// offset would wrap back inside the resource and read real data where zeros
+// are meant; and the extent of the N rows must itself fit 32 bits.
 int check_span(const char* name, fa_strides s, const fa_params* p, int dtype) {
+  FA_CHECK(check_rows(name, s, p));
   const int64_t e = (int64_t)elem_size(dtype);
-  const int64_t span = (int64_t)(p->seqlen - 1) * s.row * e + (int64_t)p->head_dim * e;
-  if (s.row * e > INT32_MAX || span > (int64_t)UINT32_MAX)
-    return fail(FA_ERR_SHAPE, "%s: one head's rows span %lld bytes (row stride %lld); the limit is 4 GiB",
-                name, (long long)span, (long long)(s.row * e));
+  const int64_t rows = ceil_div(p->seqlen, FA_MASK_BLOCK) * FA_MASK_BLOCK;
+  const int64_t span = (rows - 1) * s.row * e + (int64_t)p->head_dim * e;
+  const int64_t extent = (int64_t)(p->seqlen - 1) * s.row * e + (int64_t)p->head_dim * e;
+  if (span > ((int64_t)1 << 32) || extent > (int64_t)UINT32_MAX)
+    return fail(FA_ERR_SHAPE,
+                "%s: the %lld rows of one head's 128-row tiles span %lld bytes (row stride %lld); "
+                "the limit is 4 GiB",
+                name, (long long)rows, (long long)span, (long long)(s.row * e));
   return FA_OK;
 }
 
@@ -141,12 +167,6 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-#define FA_CHECK(expr)            \
-  do {                            \
-    const int st_ = (expr);       \
-    if (st_ != FA_OK) return st_; \
-  } while (0)
-
 }  // namespace
 
 extern "C" {
@@ -173,6 +193,8 @@ int fa_fwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   FA_CHECK(check_tensor("o", o, so, p->o_dtype));
   FA_CHECK(check_span("k", sk, p, p->dtype));
   FA_CHECK(check_span("v", sv, p, p->dtype));
+  FA_CHECK(check_rows("q", sq, p));
+  FA_CHECK(check_rows("o", so, p));
   if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
   if (tile_log && reinterpret_cast<uintptr_t>(tile_log) % 4)
@@ -221,6 +243,10 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   FA_CHECK(check_span("k", sk, p, p->dtype));
   FA_CHECK(check_span("v", sv, p, p->dtype));
   FA_CHECK(check_span("dout", sdo, p, p->dtype));
+  FA_CHECK(check_rows("o", so, p));
+  FA_CHECK(check_rows("dq", sdq, p));
+  FA_CHECK(check_rows("dk", sdk, p));
+  FA_CHECK(check_rows("dv", sdv, p));
   if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
   const size_t need = fa_bwd_workspace_size(p);

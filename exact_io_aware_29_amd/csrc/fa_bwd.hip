@@ -153,10 +153,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
 
     // This lane's key as the B operand of S = Q K^T and dP = dO V^T (V from
-    // LDS at d=128).
+    // LDS at d=128). Keys past the valid length are zero, whatever their
+    // memory holds: their P is 0, and their dK and dV come out 0.
+    const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
     bf16x8 kf[C::NKK], vf[C::VLDS ? 1 : C::NKK];
     {
-      const bool ok = my_k < p.N;
+      const bool ok = my_k < kvalid;
       const int64_t r = ok ? my_k : 0;
   #pragma unroll
       for (int kk = 0; kk < C::NKK; ++kk) {
@@ -172,7 +174,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       dvt[db] = f32x16{};
     }
 
-    const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
     if (k0 < kvalid) {  // else every key of the block is masked: dK = dV = 0
       // Steps run over (query head of the group) x (query block), limited to
       // the rows that can see a key of this block: from the causal diagonal or
@@ -236,9 +237,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         int h, q0b;
         step_unit(sidx, h, q0b);
         const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
-                                   (uint32_t)(p.N - 1) * qsb + 2 * D);
+                                   rows_extent(p.N, qsb, 2 * D));
         const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
-                                   (uint32_t)(p.N - 1) * dsb + 2 * D);
+                                   rows_extent(p.N, dsb, 2 * D));
         // Registers are at their limit with the V block in LDS: rebuild the
         // DMA offsets for this step from a lane index read afresh (an opaque
         // mbcnt, so neither it nor the offsets are hoisted out of the loop and
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         int vvo[VT::NLD];
         const int vsb = 2 * (int)a.sv.n;
         dma_offsets<D, C::BK>(vvo, vsb, w, lane);
-        const Rsrc vrs = make_rsrc(Vp, (uint32_t)(p.N - 1) * vsb + 2 * D);
+        const Rsrc vrs = make_rsrc(Vp, rows_extent(kvalid, vsb, 2 * D));
         dma_tile<D, C::BK>(vrs, vvo, (uint32_t)k0 * vsb, smem + C::VOFF, w);
       }
 
@@ -540,11 +541,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const float sl2 = p.scale_l2;
   const bool causal = p.causal != 0;
 
+  // Keys past the valid length read as zero, whatever their memory holds.
+  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
   const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;
   const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
-                             (uint32_t)(p.N - 1) * ksb + 2 * D);
+                             rows_extent(kvalid, ksb, 2 * D));
   const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
-                             (uint32_t)(p.N - 1) * vsb + 2 * D);
+                             rows_extent(kvalid, vsb, 2 * D));
   for (int rep = 0; rep < NREP; ++rep) {
     const int qb = NREP == 2 ? (rep == 0 ? nqb - 1 - ui : ui) : (causal ? nqb - 1 - ui : ui);
     if (rep == 1) {
@@ -618,7 +621,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
-    const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
     const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
     const int ntiles = (kend + C::BC - 1) / C::BC;
     const int64_t log_row =

@@ -83,10 +83,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   }
 
   const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;
+  // The cache rows past the valid length L read as zero, whatever their
+  // memory holds (a cache is often allocated uninitialised).
   const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
-                             (uint32_t)(p.N - 1) * ksb + 2 * D);
+                             rows_extent(L, ksb, 2 * D));
   const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
-                             (uint32_t)(p.N - 1) * vsb + 2 * D);
+                             rows_extent(L, vsb, 2 * D));
   int kvo[T::NLD], vvo[T::NLD];
   dma_offsets<D, C::BC>(kvo, ksb, w, lane);
   dma_offsets<D, C::BC>(vvo, vsb, w, lane);

@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
        kt = mrow.next_tile<C::BC>(kt + 1, ntiles)) {
     const int key0 = kt * C::BC;
     __syncthreads();
-    stage_rows<T, D, C::BC, C::KROW>(Kp, a.sk.n, key0, p.N, Ks, tid);
-    stage_cols<T, D, C::BC, C::VROW>(Vp, a.sv.n, key0, p.N, Vt, tid);
+    stage_rows<T, D, C::BC, C::KROW>(Kp, a.sk.n, key0, kvalid, Ks, tid);
+    stage_cols<T, D, C::BC, C::VROW>(Vp, a.sv.n, key0, kvalid, Vt, tid);
     __syncthreads();
     if (a.log && tid == 0) log_tile(a.log, log_row, key0);
 
@@ -274,13 +274,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   const int ui = L - head_lin * nunit;
   const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
 
+  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
   const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;  // row strides in bytes
   const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
-                             (uint32_t)(p.N - 1) * ksb + 2 * D);
+                             rows_extent(kvalid, ksb, 2 * D));
   const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
-                             (uint32_t)(p.N - 1) * vsb + 2 * D);
-
-  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
+                             rows_extent(kvalid, vsb, 2 * D));
   for (int rep = 0; rep < NREP; ++rep) {
     const int qb = NREP == 2 ? (rep == 0 ? nqb - 1 - ui : ui) : ui;
     if (rep == 1) {

@@ -109,12 +109,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_fp8(FwdArgs a) {
   const int my_q = q0 + 32 * w + lr;
 
   const int ksb = (int)a.sk.n, vsb = (int)a.sv.n;  // row strides in bytes
-  const Rsrc krs = make_rsrc(static_cast<const uint8_t*>(a.k) + b * a.sk.b + hk * a.sk.h,
-                             (uint32_t)(p.N - 1) * ksb + D);
-  const Rsrc vrs = make_rsrc(static_cast<const uint8_t*>(a.v) + b * a.sv.b + hk * a.sv.h,
-                             (uint32_t)(p.N - 1) * vsb + D);
-
   const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
+  const Rsrc krs = make_rsrc(static_cast<const uint8_t*>(a.k) + b * a.sk.b + hk * a.sk.h,
+                             rows_extent(kvalid, ksb, D));
+  const Rsrc vrs = make_rsrc(static_cast<const uint8_t*>(a.v) + b * a.sv.b + hk * a.sv.h,
+                             rows_extent(kvalid, vsb, D));
   const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
   const int ntiles = (kend + C::BC - 1) / C::BC;
   const int kfirst = max(0, q0 - p.wl) / C::BC;

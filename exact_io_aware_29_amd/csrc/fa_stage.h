@@ -135,6 +135,17 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t nbytes) {
                                            0x00020000);
 }
 
+// Byte extent of a resource over the first `rows` rows of one head (row
+// pitch `sb` bytes, `rb` bytes of data per row). The range check covers the
+// sum of the lane and scalar offsets, so every read at or past row `rows`
+// returns zero: key rows past a sequence's valid length are never fetched,
+// whatever their memory holds. The host guarantees that no row offset of a
+// visited tile reaches 2^32 (no wrap back into the range) and that the row
+// pitch is at least `rb` (rows do not overlap).
+__device__ __forceinline__ uint32_t rows_extent(int rows, int sb, int rb) {
+  return rows > 0 ? (uint32_t)(rows - 1) * (uint32_t)sb + (uint32_t)rb : 0u;
+}
+
 template <int D, int ROWS>
 struct SwzTile {
   static constexpr int RB = 2 * D;            // bytes per row
@@ -167,7 +178,7 @@ __device__ __forceinline__ void dma_offsets(int (&voff)[NL], int stride_bytes, i
   for (int i = 0; i < NL; ++i) {
     const int p = (i * NW + w) * 64 + lane;  // 16-byte LDS position
     const int r = p / T::CPR, pc = p % T::CPR;
-    voff[i] = r * stride_bytes + 16 * (pc ^ T::swz(r));
+    voff[i] = (int)((uint32_t)r * (uint32_t)stride_bytes + 16u * (uint32_t)(pc ^ T::swz(r)));
   }
 }
 

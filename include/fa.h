@@ -25,7 +25,10 @@
  * Masks, all combined with AND (a disallowed score counts as -infinity):
  *   causal     key j is allowed for query i iff j <= i (top-left aligned);
  *   seqlens_k  key j is allowed iff j < seqlens_k[b] (key padding); query
- *              rows past the valid length are still computed;
+ *              rows past the valid length are still computed; K and V rows
+ *              at or past the valid length are never read (the kernels
+ *              take them as zeros), so their memory may hold anything,
+ *              NaN or uninitialised values included;
  *   block_mask key j is allowed for query i iff
  *              block_mask[(i/128)*block_mask_ld + j/128] != 0; this is the
  *              block-sparse variant of the report's sections 2.6 and 3.5 at a
@@ -63,15 +66,22 @@ extern "C" {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,     /* a size is <= 0, or too large to index: this
-                          * includes one head's rows of K or V (and of Q or
-                          * dO in fa_bwd) spanning 4 GiB or more, that is
-                          * (seqlen - 1) * row stride + head_dim elements,
-                          * or a row stride of 2 GiB or more */
+  FA_ERR_SHAPE = -2,     /* a size is <= 0, or too large to index. The
+                          * kernels read K and V (and Q and dO in fa_bwd)
+                          * in tiles that cover whole 128-row blocks, through
+                          * 32-bit byte offsets from the head's first row:
+                          * R = ceil(seqlen / 128) * 128 rows are addressed,
+                          * so (R - 1) * row stride + head_dim elements must
+                          * not exceed 4 GiB (and (seqlen - 1) * row stride
+                          * + head_dim elements must stay below it) */
   FA_ERR_DTYPE = -3,     /* unsupported dtype combination */
   FA_ERR_HEADDIM = -4,   /* head_dim is not 64 or 128 */
   FA_ERR_GQA = -5,       /* heads_q is not a multiple of heads_kv */
-  FA_ERR_STRIDE = -6,    /* a stride is negative or not a multiple of 16 bytes */
+  FA_ERR_STRIDE = -6,    /* a stride is negative or not a multiple of 16
+                          * bytes, or the row stride of a [B][H][N][d]
+                          * tensor is below head_dim (rows would overlap;
+                          * fa_decode's q and o, of which only row 0 is
+                          * used, are exempt) */
   FA_ERR_ALIGN = -7,     /* a base pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = -8, /* workspace missing or smaller than required */
   FA_ERR_HIP = -9,       /* a HIP call failed (see fa_last_error_detail) */

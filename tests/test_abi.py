@@ -146,6 +146,78 @@ def test_head_span_over_4_gib_is_rejected():
 
 
 @no_gpu_only
+def test_tile_rounded_rows_bound_the_span():
+    """Tiles cover whole 128-row blocks: a tail tile addresses rows up to
+    ceil(N/128)*128 - 1, and their 32-bit byte offsets must not wrap past
+    4 GiB back into the buffer (rows past N must read as zeros)."""
+    MiB = 1 << 20
+    # forward, d=64, N=41, K row stride 100 MiB: the 41 valid rows span
+    # 40 * 100 MiB + 128 B < 4 GiB, but rows 41..127 of the tile do not fit
+    p = _params(batch=1, heads_q=1, heads_kv=1, seqlen=41, head_dim=64)
+    assert 40 * 100 * MiB + 128 < 1 << 32
+    wide = _abi.Strides(0, 0, 100 * MiB // 2)
+    st, detail = _fwd(p, sk=wide)
+    assert st == _abi.FA_ERR_SHAPE and "k:" in detail and "128-row" in detail, (st, detail)
+    st, detail = _fwd(p, sk=_abi.Strides(0, 0, 64), sq=_abi.Strides(0, 0, 64))
+    assert st != _abi.FA_ERR_SHAPE, detail
+    # backward, d=64, N=100, Q row stride 41 MiB (the dK/dV kernel stages Q)
+    p = _params(batch=1, heads_q=1, heads_kv=1, seqlen=100, head_dim=64)
+    assert 99 * 41 * MiB + 128 < 1 << 32
+    lib = fa.library()
+    s = _abi.Strides(0, 0, 64)
+    q41 = _abi.Strides(0, 0, 41 * MiB // 2)
+    for pos in range(2):  # Q, then dO
+        args = [s, s]
+        args[pos] = q41
+        st = lib.fa_bwd(ctypes.byref(p), P16, args[0], P32, s, P48, s, P64, s, P80, args[1],
+                        ctypes.c_void_p(0x6000), P16, s, P32, s, P48, s,
+                        ctypes.c_void_p(0x8000), 1 << 30, None, None, None)
+        detail = lib.fa_last_error_detail().decode()
+        assert st == _abi.FA_ERR_SHAPE and "128-row" in detail, (pos, st, detail)
+    # the largest stride that still fits: 127 rows * stride + 128 B <= 4 GiB
+    ok = ((1 << 32) - 128) // 127 // 16 * 16
+    p = _params(batch=1, heads_q=1, heads_kv=1, seqlen=41, head_dim=64)
+    assert _fwd(p, sk=_abi.Strides(0, 0, ok // 2))[0] != _abi.FA_ERR_SHAPE
+    assert _fwd(p, sk=_abi.Strides(0, 0, ok // 2 + 8))[0] == _abi.FA_ERR_SHAPE
+
+
+@no_gpu_only
+def test_overlapping_rows_are_rejected():
+    """A row stride below head_dim (e.g. a tensor expanded from one row) is
+    FA_ERR_STRIDE for every [B][H][N][d] tensor of fa_fwd and fa_bwd: rows
+    past N would otherwise read real rows where the kernels expect zeros."""
+    p = _params()
+    for key in ("sq", "sk", "so"):
+        for row in (0, 8, 56):
+            st, detail = _fwd(p, **{key: _abi.Strides(64, 64, row)})
+            assert st == _abi.FA_ERR_STRIDE and "below head_dim" in detail, (key, row, st, detail)
+    lib = fa.library()
+    s, skv = _strides(p), _strides(p, p.heads_kv)
+    zero = _abi.Strides(0, 0, 0)
+    for pos in range(9):  # q, k, v, o, dout, dq, dk, dv in order (pos 8: none)
+        st_args = [s, skv, skv, s, s, s, skv, skv]
+        if pos < 8:
+            st_args[pos] = zero
+        st = lib.fa_bwd(ctypes.byref(p), P16, st_args[0], P32, st_args[1], P48, st_args[2],
+                        P64, st_args[3], P80, st_args[4], ctypes.c_void_p(0x6000),
+                        P16, st_args[5], P32, st_args[6], P48, st_args[7],
+                        ctypes.c_void_p(0x8000), 1 << 30, None, None, None)
+        if pos < 8:
+            assert st == _abi.FA_ERR_STRIDE, (pos, st, lib.fa_last_error_detail().decode())
+        else:
+            assert st not in (_abi.FA_ERR_STRIDE, _abi.FA_ERR_SHAPE), st
+    # decode: K and V rows must not overlap; q and o (row 0 only) are exempt
+    pd = _params(heads_q=4, heads_kv=2, seqlen=300)
+    one = _abi.Strides(4 * 64, 64, 0)
+    st = lib.fa_decode(ctypes.byref(pd), P16, one, P32, zero, P48, skv, P64, one, P80,
+                       ctypes.c_void_p(0x8000), 1 << 30, None)
+    assert st == _abi.FA_ERR_STRIDE, (st, lib.fa_last_error_detail().decode())
+    st = lib.fa_decode(ctypes.byref(pd), P16, one, P32, skv, P48, skv, P64, one, P80,
+                       ctypes.c_void_p(0x8000), 1 << 30, None)
+    assert st not in (_abi.FA_ERR_STRIDE, _abi.FA_ERR_SHAPE), st
+
+
+@no_gpu_only
 def test_fwd_rejects_bad_pointers_and_strides():
     p = _params()
     assert _fwd(p, q=ctypes.c_void_p(0))[0] == _abi.FA_ERR_NULL
