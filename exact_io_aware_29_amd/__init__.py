@@ -21,7 +21,8 @@ import torch
 from . import _abi
 from ._abi import FA_BF16, FA_FP32, FA_MASK_BLOCK, Params, Strides  # noqa: F401
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_decode", "fa_bwd_workspace_size", "fa_decode_workspace_size",
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_decode", "fa_bwd_workspace_size",
+           "fa_decode_workspace_size",
            "fa_tile_log_words", "fa_strerror",
            "FAError", "make_params", "library"]
 
@@ -203,6 +204,32 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
     if st != 0:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv, log
+
+
+def fa_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                   lse: torch.Tensor, dout: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor,
+                   dv: torch.Tensor, *, scale: Optional[float] = None, causal: bool = False,
+                   seqlens_k: Optional[torch.Tensor] = None,
+                   block_mask: Optional[torch.Tensor] = None,
+                   tile_log: Optional[torch.Tensor] = None, window: Optional[tuple] = None,
+                   dropout_p: float = 0.0, dropout_seed: int = 0, dropout_offset: int = 0):
+    """Backward pass that allocates nothing: the caller passes the outputs
+    (and, optionally, a caller-zeroed int32 tile log of
+    2 * fa_tile_log_words words), and the library's fixed device array
+    serves as workspace (up to FA_NOALLOC_WORKSPACE_BYTES). Calls that can
+    overlap on one GPU share that array and race."""
+    lib = _abi.load()
+    p = _params_from(q, k, scale=scale, causal=causal, seqlens_k=seqlens_k,
+                     block_mask=block_mask, o_dtype=o.dtype, window=window,
+                     dropout_p=dropout_p, dropout_seed=dropout_seed,
+                     dropout_offset=dropout_offset)
+    st = lib.fa_bwd_noalloc(ctypes.byref(p), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                            _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout),
+                            _ptr(lse), _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv),
+                            _strides(dv), _ptr(tile_log), None, _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd_noalloc")
+    return dq, dk, dv
 
 
 def fa_decode_workspace_size(params: Params) -> int:

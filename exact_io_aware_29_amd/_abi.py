@@ -27,6 +27,7 @@ FA_BF16 = 0
 FA_FP32 = 1
 FA_FP8_E4M3 = 2
 FA_MASK_BLOCK = 128
+FA_NOALLOC_WORKSPACE_BYTES = 32 << 20
 
 
 class Strides(ctypes.Structure):
@@ -68,6 +69,8 @@ SIGNATURES = {
     "fa_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
     "fa_bwd": (ctypes.c_int, [ctypes.POINTER(Params), _P, _S, _P, _S, _P, _S, _P, _S, _P, _S, _P,
                               _P, _S, _P, _S, _P, _S, _P, ctypes.c_size_t, _P, _P, _P]),
+    "fa_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Params), _P, _S, _P, _S, _P, _S, _P, _S, _P,
+                                      _S, _P, _P, _S, _P, _S, _P, _S, _P, _P, _P]),
     "fa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Params)]),
     "fa_decode": (ctypes.c_int, [ctypes.POINTER(Params), _P, _S, _P, _S, _P, _S, _P, _S, _P, _P,
                                  ctypes.c_size_t, _P]),

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip",
+           "fa_scratch.hip"]
 # Per-source extra flags. Matrix-core results go to VGPRs (the softmax reads
 # them directly, without v_accvgpr_read); the register allocator then uses
 # AGPRs as overflow for long-lived values.

@@ -223,11 +223,19 @@ int fa_fwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   return FA_OK;
 }
 
-int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
-           const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,
-           fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk, fa_strides sdk,
-           void* dv, fa_strides sdv, void* workspace, size_t workspace_bytes, uint32_t* tile_log,
-           void* const* stage_events, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_bwd and fa_bwd_noalloc: the same checks, then the same two kernels.
+// With `own_scratch` the workspace is the library's fixed device array
+// (looked up only after every argument check has passed).
+int bwd_call(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+             const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,
+             fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk,
+             fa_strides sdk, void* dv, fa_strides sdv, bool own_scratch, void* workspace,
+             size_t workspace_bytes, uint32_t* tile_log, void* const* stage_events,
+             void* stream) {
   g_detail[0] = '\0';
   FA_CHECK(check_params(p));
   if (p->dtype != FA_BF16) return fail(FA_ERR_DTYPE, "the backward pass supports bf16 inputs only");
@@ -250,16 +258,29 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   if (!lse) return fail(FA_ERR_NULL, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(FA_ERR_ALIGN, "lse is not 4-byte aligned");
   const size_t need = fa_bwd_workspace_size(p);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (reinterpret_cast<uintptr_t>(workspace) % 16)
-    return fail(FA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (own_scratch) {
+    if (need > FA_NOALLOC_WORKSPACE_BYTES)
+      return fail(FA_ERR_WORKSPACE,
+                  "the backward needs %zu bytes of workspace; the fixed array holds %zu "
+                  "(batch * heads_q * seqlen above %zu)",
+                  need, (size_t)FA_NOALLOC_WORKSPACE_BYTES,
+                  (size_t)FA_NOALLOC_WORKSPACE_BYTES / (2 * sizeof(float)));
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16)
+      return fail(FA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  }
   if (tile_log && reinterpret_cast<uintptr_t>(tile_log) % 4)
     return fail(FA_ERR_ALIGN, "tile_log is not 4-byte aligned");
   if (stage_events)
     for (int i = 0; i < 3; ++i)
       if (!stage_events[i]) return fail(FA_ERR_NULL, "stage_events[%d] is NULL", i);
+
+  hipError_t e;
+  if (own_scratch && (e = fa::scratch_address(&workspace)) != hipSuccess)
+    return hip_fail(e, "scratch array address");
 
   fa::BwdArgs a;
   a.p = make_problem(p);
@@ -291,7 +312,6 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   auto mark = [&](int i) -> hipError_t {
     return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) : hipSuccess;
   };
-  hipError_t e;
   // dQ first: it also writes the row statistics the dK/dV kernel reads.
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = fa::launch_bwd_dq(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_dq launch");
@@ -299,6 +319,28 @@ int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_s
   if ((e = fa::launch_bwd_dkdv(a, p->head_dim, s)) != hipSuccess) return hip_fail(e, "bwd_dkdv launch");
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event record");
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const fa_params* p, const void* q, fa_strides sq, const void* k, fa_strides sk,
+           const void* v, fa_strides sv, const void* o, fa_strides so, const void* dout,
+           fa_strides sdo, const float* lse, void* dq, fa_strides sdq, void* dk, fa_strides sdk,
+           void* dv, fa_strides sdv, void* workspace, size_t workspace_bytes, uint32_t* tile_log,
+           void* const* stage_events, void* stream) {
+  return bwd_call(p, q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv, false,
+                  workspace, workspace_bytes, tile_log, stage_events, stream);
+}
+
+int fa_bwd_noalloc(const fa_params* p, const void* q, fa_strides sq, const void* k,
+                   fa_strides sk, const void* v, fa_strides sv, const void* o, fa_strides so,
+                   const void* dout, fa_strides sdo, const float* lse, void* dq, fa_strides sdq,
+                   void* dk, fa_strides sdk, void* dv, fa_strides sdv, uint32_t* tile_log,
+                   void* const* stage_events, void* stream) {
+  return bwd_call(p, q, sq, k, sk, v, sv, o, so, dout, sdo, lse, dq, sdq, dk, sdk, dv, sdv, true,
+                  nullptr, 0, tile_log, stage_events, stream);
 }
 
 namespace {

@@ -89,4 +89,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s);
 
+// Device address of the library's fixed scratch array on the current device
+// (looked up once per device); it holds FA_NOALLOC_WORKSPACE_BYTES.
+hipError_t scratch_address(void** out);
+
 }  // namespace fa

@@ -237,6 +237,45 @@ int fa_bwd(const fa_params* p,
            void* const* stage_events,
            void* stream);
 
+/* Size of the library's fixed device array that serves as fa_bwd_noalloc's
+ * workspace: 32 MiB per GPU, enough for batch * heads_q * seqlen up to
+ * 4194304 rows (fa_bwd_workspace_size(p) <= this). */
+#define FA_NOALLOC_WORKSPACE_BYTES (32u << 20)
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid hipMalloc. It takes no workspace argument and calls no allocator;
+ * the two fp32 row vectors that fa_bwd keeps in the caller's workspace live
+ * in a fixed device array inside the library instead, of
+ * FA_NOALLOC_WORKSPACE_BYTES, which each GPU the library runs on holds
+ * until the process ends. Its address is looked up once per device (with
+ * that device current) on the first call there, so the stream must belong
+ * to the current device.
+ *
+ * Arguments, outputs and errors as fa_bwd, without workspace and
+ * workspace_bytes; a problem with fa_bwd_workspace_size(p) above
+ * FA_NOALLOC_WORKSPACE_BYTES is FA_ERR_WORKSPACE (host check, before any
+ * HIP call). Nothing in the array needs clearing: every call writes the
+ * row vectors before it reads them. Every call on one GPU shares that
+ * array, so calls that can overlap on one GPU (different streams without an
+ * ordering between them) race and give wrong results; calls on one stream,
+ * or ordered by events, are safe. Results are bit-identical to fa_bwd's.
+ */
+int fa_bwd_noalloc(const fa_params* p,
+                   const void* q, fa_strides sq,
+                   const void* k, fa_strides sk,
+                   const void* v, fa_strides sv,
+                   const void* o, fa_strides so,
+                   const void* dout, fa_strides sdo,
+                   const float* lse,
+                   void* dq, fa_strides sdq,
+                   void* dk, fa_strides sdk,
+                   void* dv, fa_strides sdv,
+                   uint32_t* tile_log,
+                   void* const* stage_events,
+                   void* stream);
+
 /* Bytes of device workspace fa_decode needs for `p` (0 when the keys are
  * not split; 0 also for invalid parameters). */
 size_t fa_decode_workspace_size(const fa_params* p);

@@ -257,6 +257,33 @@ def test_bwd_validation():
     assert "stage_events" in lib.fa_last_error_detail().decode()
 
 
+@no_gpu_only
+def test_bwd_noalloc_rejects_problems_beyond_its_array():
+    """fa_bwd_noalloc's workspace is the library's fixed array: a problem
+    whose two row vectors need more than FA_NOALLOC_WORKSPACE_BYTES is
+    FA_ERR_WORKSPACE, decided on the host before any HIP call."""
+    lib = fa.library()
+    assert _abi.FA_NOALLOC_WORKSPACE_BYTES == 32 << 20
+    rows_max = _abi.FA_NOALLOC_WORKSPACE_BYTES // 8  # two fp32 values per row
+    for seqlen, ok in ((rows_max // 16, True), (rows_max // 16 + 1, False)):
+        p = _params(batch=1, heads_q=16, heads_kv=16, seqlen=seqlen)
+        s = _strides(p)
+        st = lib.fa_bwd_noalloc(ctypes.byref(p), P16, s, P32, s, P48, s, P64, s, P80, s,
+                                ctypes.c_void_p(0x6000), P16, s, P32, s, P48, s, None, None, None)
+        detail = lib.fa_last_error_detail().decode()
+        if ok:
+            assert st != _abi.FA_ERR_WORKSPACE, (seqlen, st, detail)
+        else:
+            assert st == _abi.FA_ERR_WORKSPACE and "fixed array" in detail, (seqlen, st, detail)
+    # the other checks are fa_bwd's
+    p = _params()
+    s = _strides(p)
+    st = lib.fa_bwd_noalloc(ctypes.byref(p), P16, s, P32, _abi.Strides(0, 0, 0), P48, s, P64, s,
+                            P80, s, ctypes.c_void_p(0x6000), P16, s, P32, s, P48, s, None, None,
+                            None)
+    assert st == _abi.FA_ERR_STRIDE
+
+
 def test_size_queries():
     p = _params(seqlen=4097)
     nlb = 33

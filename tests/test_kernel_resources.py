@@ -24,7 +24,8 @@ import pytest
 
 from exact_io_aware_29_amd import build as B
 
-HIP_SOURCES = [s for s in B.SOURCES if s.endswith(".hip")]
+HIP_SOURCES = [s for s in B.SOURCES
+               if s.endswith(".hip") and "__global__" in open(os.path.join(B.CSRC, s)).read()]
 needs_hipcc = pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC),
                                  reason="hipcc not available")
 
