@@ -50,6 +50,13 @@ def parse_args():
                     help="workload id (2 = the headline B64 H16 N1024 d64 shape; 7 = decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--no-north-star", action="store_true",
+                    help="with the default workload, skip the north_star_c3 record (the causal "
+                         "key-padded B8 H16 N4096 d128 workload measured in the same run)")
+    ap.add_argument("--c3-steps", type=int, default=20,
+                    help="timed steps of the north_star_c3 measurement")
+    ap.add_argument("--c3-warmup", type=int, default=5,
+                    help="untimed warmup steps of the north_star_c3 measurement")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -389,8 +396,6 @@ def main():
         io_sweep(args)
         return
 
-    import exact_io_aware_29_amd as fa
-    from exact_io_aware_29_amd import accounting as acc
     from synth import WORKLOADS, draw
 
     w = WORKLOADS[args.workload]
@@ -399,6 +404,68 @@ def main():
     if w.decode:
         decode_main(args, w, inp, dev)
         return
+    rec = measure(args, args.workload, w, inp, dev, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        per_b = rec.pop("_per_b")
+        rec["cpu_baseline"] = cpu_baseline(inp, per_b, args.cpu_seconds)
+    rec.pop("_per_b", None)
+    del inp
+    if args.workload == 2 and not args.no_north_star:
+        rec["north_star_c3"] = north_star_c3(args, dev)
+    print(json.dumps(rec), flush=True)
+
+
+# Targets of the causal key-padded B8 H16 N4096 d128 configuration: the
+# forward at >= 50 % and forward + backward at >= 35 % of the bf16 dense
+# matrix-core peak.
+C3_TARGET_PCT = {"fwd": 50.0, "fwd_bwd": 35.0}
+
+
+def north_star_c3(args, dev):
+    """The causal, key-padded B8 H16 N4096 d128 bf16 workload (workload 3),
+    measured in the same run as the headline line: forward and
+    forward + backward time, TFLOP/s and % of the bf16 peak, each kernel's
+    time and roofline fraction, and whether the targets are met."""
+    from synth import WORKLOADS, draw
+
+    w = WORKLOADS[3]
+    inp = draw(w, 3)
+    r = measure(args, 3, w, inp, dev, args.c3_steps, args.c3_warmup)
+    del inp
+    k = r["kernels"]
+    fwd_ms = k["fwd"]["ms"]
+    fb_ms = sum(v["ms"] for v in k.values())
+    fwd_pct = 100 * r["fwd_tflops"] / k["fwd"]["peak"]
+    fb_tf = r["algorithmic_flop"]["fwd_bwd"] / (fb_ms * 1e-3) / 1e12
+    fb_pct = 100 * fb_tf / k["fwd"]["peak"]
+    return {
+        "workload": r["config"]["workload"],
+        "steps": args.c3_steps, "warmup": args.c3_warmup,
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": r["fwd_tflops"],
+        "pct_of_peak_fwd": round(fwd_pct, 2),
+        "fwd_bwd_ms": round(fb_ms, 4),
+        "fwd_bwd_tflops": round(fb_tf, 1),
+        "pct_of_peak_fwd_bwd": round(fb_pct, 2),
+        "ms_per_step_wall": r["ms_per_step"],
+        "kernels": {n: {"ms": v["ms"], "achieved": v["achieved"], "frac": v["frac"]}
+                    for n, v in k.items()},
+        "dominant_kernel": r["roofline"]["kernel"],
+        "dominant_frac": r["roofline"]["frac"],
+        "target_pct": C3_TARGET_PCT,
+        "target_met": {"fwd": fwd_pct >= C3_TARGET_PCT["fwd"],
+                       "fwd_bwd": fb_pct >= C3_TARGET_PCT["fwd_bwd"]},
+    }
+
+
+def measure(args, workload_id, w, inp, dev, steps, warmup):
+    """Time `steps` steps of one workload (after `warmup` untimed ones) and
+    return the bench record without the CPU baseline."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_29_amd as fa
+    from exact_io_aware_29_amd import accounting as acc
 
     def t(a):
         if w.dtype == "bf16":
@@ -435,11 +502,11 @@ def main():
             fa.fa_bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws,
                       stage_events=None if ev is None else ev[2:5], **kw)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for ev in events:
         for e in ev:
             e.record()  # create the events outside the timed region
@@ -448,7 +515,7 @@ def main():
     scratch = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
                if args.flush_mib else None)
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         if scratch is not None:
             scratch.fill_(float(i))  # evicts L2 and MALL between steps
         step(events[i])
@@ -458,7 +525,7 @@ def main():
     copy_calibration(args, dev)
 
     def times(a, b):
-        return np.array([events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)])
+        return np.array([events[i][a].elapsed_time(events[i][b]) for i in range(steps)])
 
     spans = {"fwd": (0, 1)}
     if w.backward:
@@ -471,7 +538,7 @@ def main():
         block_mask=inp.block_mask, window=w.window).sum()) for b in range(w.batch)]
     pairs = sum(per_b) * w.heads_q
     fl = acc.flops(pairs, w.head_dim)
-    ms_step = wall / args.steps * 1e3
+    ms_step = wall / steps * 1e3
     if scratch is not None:  # the scratch writes are not part of a step
         ms_step = sum(kern_ms.values())
     step_flop = fl["fwd_bwd"] if w.backward else fl["fwd"]
@@ -496,7 +563,7 @@ def main():
     roofline = {"kernel": dom, "bound": dk_["bound"], "achieved": dk_["achieved"],
                 "peak": dk_["peak"], "unit": dk_["unit"], "frac": dk_["frac"],
                 "traffic": recorded_traffic("fwd_fp8" if w.dtype == "fp8" and dom == "fwd"
-                                            else dom, args.workload)}
+                                            else dom, workload_id)}
 
     fwd_tf = fl["fwd"] / (kern_ms["fwd"] * 1e-3) / 1e12
     rec = {
@@ -504,8 +571,8 @@ def main():
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -529,9 +596,11 @@ def main():
     if scratch is not None:
         rec["flush_mib"] = args.flush_mib
         rec["timing"] = "sum of kernel event times; scratch written between steps"
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, per_b, args.cpu_seconds)
-    print(json.dumps(rec), flush=True)
+    rec["_per_b"] = per_b
+    del q, k, v, do, o, lse
+    if w.backward:
+        del dq, dk, dv, ws
+    return rec
 
 
 if __name__ == "__main__":
