@@ -78,14 +78,33 @@ SIGNATURES = {
     "fa_last_error_detail": (ctypes.c_char_p, []),
 }
 
+PARANOID_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                 "libfa_paranoid.so")
+
 _lib = None
 
 
+def load_variant(path: str) -> ctypes.CDLL:
+    """A separately loaded build of the same ABI (the debug build with extra
+    barriers); the caller keeps the handle."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is missing: build it first")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfa.so once; raise RuntimeError (never fall back) if absent."""
+    """Load libfa.so once; raise RuntimeError (never fall back) if absent.
+    The environment variable FA_LIBRARY names another build of the same
+    library to load instead (the tests use it for the host-sanitizer build)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = os.environ.get("FA_LIBRARY", path)
     if not os.path.exists(path):
         raise RuntimeError(
             f"HIP library {path} is missing: build it with `python -m exact_io_aware_29_amd.build`")

@@ -40,31 +40,82 @@ FLAGS = [
 KERNEL_FLAGS = ["-fno-honor-nans"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+# The debug variant: a workgroup barrier before every refill of an LDS stage
+# and a full wait plus barrier right after it (FA_PARANOID_BARRIERS in
+# fa_stage.h). Its results must equal the release library's bit for bit;
+# the GPU tests compare the two. Nothing else loads it.
+PARANOID_OUT = os.path.join(PKG, "libfa_paranoid.so")
+PARANOID_FLAGS = ["-DFA_PARANOID_BARRIERS=1"]
+
+
+def _compile(job) -> str:
+    src, variant = job
+    objdir = os.path.join(OBJDIR, variant) if variant else OBJDIR
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip", *KERNEL_FLAGS] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = PARANOID_FLAGS if variant == "paranoid" else []
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libfa.so``; returns its path."""
-    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
-        raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(OBJDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+# Host-sanitizer build of the C ABI layer, for the CPU tests: fa_api.cpp (all
+# host code: argument checks and launches) compiled by g++ with AddressSanitizer
+# and UndefinedBehaviorSanitizer, linked with the release kernel objects. The
+# CPU test suite loads it (FA_LIBRARY) with the sanitizer runtime preloaded.
+SANITIZED_OUT = os.path.join(OBJDIR, "libfa_sanitized.so")
+ASAN_RUNTIME = "/usr/lib/x86_64-linux-gnu/libasan.so.6"
+_SAN = "-fsanitize=address,undefined"
+
+
+def build_sanitized(verbose: bool = False):
+    """Build SANITIZED_OUT from the release objects (call after build());
+    returns its path, or None when g++ or the sanitizer runtime is absent."""
+    if shutil.which("g++") is None or not os.path.exists(ASAN_RUNTIME):
+        return None
+    obj = os.path.join(OBJDIR, "fa_api_sanitized.o")
+    cc = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fPIC", _SAN,
+          "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+          "-c", os.path.join(CSRC, "fa_api.cpp"), "-o", obj]
+    kernels = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o")
+               for s in SOURCES if s != "fa_api.cpp"]
+    ld = ["g++", "-shared", _SAN, obj, *kernels, "-L/opt/rocm/lib", "-lamdhip64",
+          "-Wl,-rpath,/opt/rocm/lib", "-o", SANITIZED_OUT]
+    for cmd in (cc, ld):
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized build failed:\n{r.stdout}\n{r.stderr}")
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {SANITIZED_OUT}")
+    return SANITIZED_OUT
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``libfa.so`` and the debug variant
+    ``libfa_paranoid.so``; returns the path of ``libfa.so``."""
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(os.path.join(OBJDIR, "paranoid"), exist_ok=True)
+    jobs = [(s, "") for s in SOURCES] + [(s, "paranoid") for s in SOURCES]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PARANOID_OUT)
+    if verbose:
+        print(f"built {OUT} and {PARANOID_OUT}")
+    build_sanitized(verbose)
     return OUT
 
 

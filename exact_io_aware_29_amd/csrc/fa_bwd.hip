@@ -305,7 +305,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
           for (int kk = 0; kk < C::NKK; ++kk) roff[kk] = roff_k[kk];
         }
         const int nx = next_step(sidx + 1);
-        if (nx < nsteps) issue(nx, fill);  // lands during this step
+        if (nx < nsteps) {  // lands during this step
+          paranoid_before_fill();
+          issue(nx, fill);
+          paranoid_after_fill();
+        }
         // Dropout keep bits of this lane's key for every row of the step, made
         // before the score products so that the generator's temporaries never
         // share the registers with the S and dP accumulators (the empty asm
@@ -649,7 +653,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const char* Vs = Ks + T::BYTES;
       const int key0 = kt * C::BC;
       const int nxt = next_visit(kt + 1);
-      if (nxt < ntiles) issue(nxt, fill);
+      if (nxt < ntiles) {
+        paranoid_before_fill();
+        issue(nxt, fill);
+        paranoid_after_fill();
+      }
       if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
       const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
                              (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);

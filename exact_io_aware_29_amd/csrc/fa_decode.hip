@@ -128,7 +128,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
   // reads do not wait for that DMA; the explicit wait and barrier end it).
   auto tile = [&](int t, const char* __restrict__ ks, char* __restrict__ fill) {
     const char* vs = ks + T::BYTES;
-    if (t + 1 < ntiles) issue(t + 1, fill);
+    if (t + 1 < ntiles) {
+      paranoid_before_fill();
+      issue(t + 1, fill);
+      paranoid_after_fill();
+    }
     f32x4 sc = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) sc = mfma16k32(lds_row(ks, koff[kk]), qf[kk], sc);

@@ -340,7 +340,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
       const char* Vs = Ks + T::BYTES;
       const int key0 = kt * C::BC;
       const int nxt = next_visit(kt + 1);
-      if (nxt < ntiles) issue(nxt, fill);  // lands while this tile is computed
+      if (nxt < ntiles) {  // lands while this tile is computed
+        paranoid_before_fill();
+        issue(nxt, fill);
+        paranoid_after_fill();
+      }
       if (a.log && tid == 0) log_tile(a.log, log_row, key0);
       const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
                              (key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr);

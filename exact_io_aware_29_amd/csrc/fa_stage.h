@@ -196,6 +196,26 @@ __device__ __forceinline__ void dma_tile(Rsrc rs, const int* voff, uint32_t soff
 // This wave's DMA loads have landed in LDS.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Debug build (FA_PARANOID_BARRIERS=1): a workgroup barrier before every
+// refill of an LDS stage (every wave has finished reading it), and a full
+// wait plus barrier right after the refill is issued (it has landed for
+// every wave before anything else runs). Results must be bit-identical to
+// the release build, which overlaps the refill with the reads of the other
+// stage and relies on restrict-qualified stage pointers to keep the two
+// apart. In the release build both calls compile to nothing.
+#ifndef FA_PARANOID_BARRIERS
+#define FA_PARANOID_BARRIERS 0
+#endif
+__device__ __forceinline__ void paranoid_before_fill() {
+  if (FA_PARANOID_BARRIERS) __syncthreads();
+}
+__device__ __forceinline__ void paranoid_after_fill() {
+  if (FA_PARANOID_BARRIERS) {
+    wait_dma();
+    __syncthreads();
+  }
+}
+
 // Lane index of a wave64, computed by an opaque mbcnt pair: the compiler
 // cannot hoist or share it, so values derived from it in a loop are rebuilt
 // there instead of being kept live (or spilled) across iterations.
