@@ -502,6 +502,314 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
   }  // q-blocks of this workgroup
 }
 
+// ------------------------------------------------------ bf16, 16x16x32 MFMA
+//
+// The lean forward (no block mask, no window, no dropout) on the
+// v_mfma_f32_16x16x32_bf16 matrix instruction. Under the board's power
+// limit a 16x16x32 product costs less energy per flop than a 32x32x16 one
+// (it moves a quarter of the accumulator registers for half the flops), and
+// the clock the limit allows rises accordingly. The tiling and staging are
+// those of fwd_kernel_bf16: 128 query rows per workgroup, 32 per wave (two
+// 16-row blocks), K/V tiles of 64 keys (four 16-key blocks) double-buffered
+// in LDS by DMA.
+//
+// Layout of one 16x16x32 product (per lane l, i = l mod 16, g = l / 16):
+// A supplies row i with K slots 8 g .. 8 g + 7, B column i with the same K
+// slots, and the result holds column i, rows 4 g .. 4 g + 3. So with
+//   S^T = K Q^T   (A: key rows from LDS, B: the lane's query rows)
+// a lane holds, for each of its two query rows, keys 4 g .. 4 g + 3 of each
+// 16-key block; taking the key blocks 2 c and 2 c + 1 together, those eight
+// values are exactly a B operand of
+//   O^T += V^T P~^T   (A: V^T from two transposing reads of 4 keys each)
+// so P~ never leaves the registers. A row's 16 values per tile are spread
+// over the 4 lanes i, i + 16, i + 32, i + 48: the row maximum and the row
+// sum finish with two lane swaps (permlane16 and permlane32).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// All-reduce over the four lanes i, i + 16, i + 32, i + 48.
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+struct FwdM {
+  static constexpr int BR = 128;    // rows per workgroup (4 waves x 2 blocks of 16)
+  static constexpr int BC = 64;     // keys per tile (4 blocks of 16)
+  static constexpr int NKB = BC / 16;
+  static constexpr int NDC = D / 32;  // 32-wide head-dim chunks of the S products
+  static constexpr int NDB = D / 16;  // 16-wide head-dim blocks of O^T
+  using T = SwzTile<D, BC>;
+  static constexpr float kLag = 8.f;
+};
+
+template <int D, int NREP>
+__global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
+  using C = FwdM<D>;
+  using T = typename C::T;
+  __shared__ __attribute__((aligned(1024))) char smem[2][2 * T::BYTES];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+
+  const int nqb = (p.N + C::BR - 1) / C::BR;
+  static_assert(NREP == 1 || NREP == 2, "one block or a pair");
+  const int nunit = NREP == 2 ? (nqb + 1) / 2 : nqb;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head_lin = L / nunit;
+  const int ui = L - head_lin * nunit;
+  const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
+
+  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
+  const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;
+  const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
+                             rows_extent(kvalid, ksb, 2 * D));
+  const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
+                             rows_extent(kvalid, vsb, 2 * D));
+  const float sl2 = p.scale_l2;
+
+  for (int rep = 0; rep < NREP; ++rep) {
+    const int qb = NREP == 2 ? (rep == 0 ? nqb - 1 - ui : ui) : ui;
+    if (rep == 1) {
+      if (qb == nqb - 1 - ui) break;  // the middle block of an odd count
+      __syncthreads();                // the first block's last tile is no longer read
+    }
+    const int q0 = qb * C::BR;
+    const int r0 = q0 + 32 * w;  // first row of this wave
+    const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
+    const int ntiles = (kend + C::BC - 1) / C::BC;
+
+    // The lane's two query rows r0 + li and r0 + 16 + li as B operands:
+    // head-dim chunk dc, slots 8 lg .. 8 lg + 7.
+    bf16x8 qf[2][C::NDC];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = r0 + 16 * rb + li;
+      const bool ok = row < p.N;
+      const bf16* qrow = static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h +
+                         (int64_t)(ok ? row : 0) * a.sq.n + 8 * lg;
+#pragma unroll
+      for (int dc = 0; dc < C::NDC; ++dc) qf[rb][dc] = frag_g(qrow + 32 * dc, ok);
+    }
+    int kvo[T::NLD], vvo[T::NLD];
+    dma_offsets<D, C::BC>(kvo, ksb, w, lane);
+    dma_offsets<D, C::BC>(vvo, vsb, w, lane);
+    // K operand of key block kb, chunk dc: key row 16 kb + li, 16-byte chunk
+    // 4 dc + lg; the swizzle depends on the row's low 4 bits only, so block
+    // kb adds 16 kb rows as an immediate.
+    int koff[C::NDC];
+#pragma unroll
+    for (int dc = 0; dc < C::NDC; ++dc) koff[dc] = T::off(li, 4 * dc + lg);
+    // V^T operand of head-dim block db (rows 16 db + li of the result): the
+    // transposing read of lane 4 e + a of group lg loads key row 4 lg + e
+    // (+ 16 for the second read, + 32 c for key slice c, both immediates) at
+    // head-dim 16 db + 4 a.
+    int voff[C::NDB];
+    {
+      const int rr = 4 * lg + (li >> 2), aa = li & 3;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int d = 16 * db + 4 * aa;
+        voff[db] = rr * T::RB + 16 * ((d >> 3) ^ T::swz(rr)) + 2 * (d & 7);
+      }
+    }
+
+    f32x4 acc[C::NDB][2];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[db][0] = acc[db][1] = f32x4{};
+    float m_ref[2] = {-kInf, -kInf};  // exponent references of the two rows (log2 units)
+    float l_run[2] = {0.f, 0.f};      // this lane's share of each row's exp-sum
+    const int64_t log_row =
+        a.log ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+
+    auto issue = [&](int kt, char* stage) {
+      dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
+      dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
+    };
+    int kt = 0;
+    if (kt < ntiles) {
+      issue(kt, smem[0]);
+      wait_dma();
+      __syncthreads();
+    }
+    auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
+      const char* Vs = Ks + T::BYTES;
+      const int key0 = kt * C::BC;
+      const int nxt = kt + 1;
+      if (nxt < ntiles) {
+        paranoid_before_fill();
+        issue(nxt, fill);
+        paranoid_after_fill();
+      }
+      if (a.log && tid == 0) log_tile(a.log, log_row, key0);
+      const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+      // Causal pairs: a wave whose rows all lie above the tile's keys skips it
+      // (every score -inf, P~ = 0: m, l and O come out bit-identical).
+      const bool wave_off = NREP == 2 && key0 > r0 + 31;
+      if (!wave_off) {
+        f32x4 s[C::NKB][2];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) s[kb][0] = s[kb][1] = f32x4{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int dc = 0; dc < C::NDC; ++dc)
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) {
+            const bf16x8 kf = lds_row(Ks + 16 * kb * T::RB, koff[dc]);
+            s[kb][0] = mfma16(kf, qf[0][dc], s[kb][0]);
+            s[kb][1] = mfma16(kf, qf[1][dc], s[kb][1]);
+          }
+        {
+          // Operand reads PF ahead of the products (two products per read).
+          constexpr int NR = C::NDC * C::NKB, PF = D == 64 ? 2 : 4;
+          __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+          for (int i = 0; i < NR - PF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        if (__builtin_expect(need_mask, false)) {
+          // Register r of key block kb is key key0 + 16 kb + 4 lg + r; row
+          // r0 + 16 rb + li sees keys up to itself (causal) below kvalid.
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 16 * kb + 4 * lg + r;
+                const int row = r0 + 16 * rb + li;
+                const bool kill = (p.causal && key > row) || key >= kvalid;
+                s[kb][rb][r] = kill ? -kInf : s[kb][rb][r];
+              }
+        }
+        float mx[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float m4 = fmaxf(fmaxf(s[0][rb][0], s[0][rb][1]), fmaxf(s[0][rb][2], s[0][rb][3]));
+#pragma unroll
+          for (int kb = 1; kb < C::NKB; ++kb)
+            m4 = fmaxf(m4, fmaxf(fmaxf(s[kb][rb][0], s[kb][rb][1]),
+                                 fmaxf(s[kb][rb][2], s[kb][rb][3])));
+          mx[rb] = quad_max(m4) * sl2;
+        }
+        if (wave_any(mx[0] > m_ref[0] + C::kLag || mx[1] > m_ref[1] + C::kLag)) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float m_new = fmaxf(m_ref[rb], mx[rb]);
+            const float alpha =
+                m_new == -kInf ? 1.f : __builtin_amdgcn_exp2f(m_ref[rb] - m_new);
+            m_ref[rb] = m_new;
+            l_run[rb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[db][rb][r] *= alpha;
+          }
+        }
+        const float mu0 = m_ref[0] == -kInf ? 0.f : m_ref[0];
+        const float mu1 = m_ref[1] == -kInf ? 0.f : m_ref[1];
+        // Per 32-key slice c: exponentials of key blocks 2 c, 2 c + 1, then
+        // the PV products of the slice (the next slice's exponentials can run
+        // under them).
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          bf16x8 pf[2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float mu = rb ? mu1 : mu0;
+            float ps = 0.f;
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(s[2 * c + hb][rb][r], sl2, -mu));
+                ps += e;
+                pf[rb][4 * hb + r] = (bf16)e;
+              }
+            l_run[rb] += ps;
+          }
+          __builtin_amdgcn_s_setprio(1);
+          const char* vp = Vs + 32 * c * T::RB;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const bf16x8 vf = lds_tr(vp, voff[db], voff[db] + 16 * T::RB);
+            acc[db][0] = mfma16(vf, pf[0], acc[db][0]);
+            acc[db][1] = mfma16(vf, pf[1], acc[db][1]);
+          }
+          {
+            // PF operands (2 PF transposing reads) ahead of the products.
+            constexpr int PF = D == 64 ? 2 : 4;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+            for (int i = 0; i < C::NDB - PF; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * PF, 0);
+          }
+          __builtin_amdgcn_s_setprio(0);
+        }
+      }  // !wave_off
+      if (nxt < ntiles) {
+        wait_dma();
+        __syncthreads();  // next tile landed everywhere; this tile is no longer read
+      }
+      kt = nxt;
+    };
+    while (kt < ntiles) {
+      tile(smem[0], smem[1]);
+      if (kt >= ntiles) break;
+      tile(smem[1], smem[0]);
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = r0 + 16 * rb + li;
+      const float l_tot = quad_sum(l_run[rb]);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (row < p.N) {
+        char* obase = static_cast<char*>(a.o);
+        const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)row * a.so.n;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const int d0 = 16 * db + 4 * lg;
+          const float v0 = acc[db][rb][0] * inv, v1 = acc[db][rb][1] * inv;
+          const float v2 = acc[db][rb][2] * inv, v3 = acc[db][rb][3] * inv;
+          if (a.o_fp32) {
+            *reinterpret_cast<float4*>(obase + (orow + d0) * 4) = make_float4(v0, v1, v2, v3);
+          } else {
+            bf16x4 pk;
+            pk[0] = (bf16)v0;
+            pk[1] = (bf16)v1;
+            pk[2] = (bf16)v2;
+            pk[3] = (bf16)v3;
+            *reinterpret_cast<bf16x4*>(obase + (orow + d0) * 2) = pk;
+          }
+        }
+        if (lg == 0) {
+          const float lse = l_tot > 0.f ? (m_ref[rb] + __log2f(l_tot)) * kLn2 : -kInf;
+          a.lse[((int64_t)b * p.Hq + h) * p.N + row] = lse;
+        }
+      }
+    }
+  }  // q-blocks of this workgroup
+}
+
 // fp32 inputs (reference-precision path) use the generic kernel above.
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
@@ -511,11 +819,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Lean launches (no mask, window or dropout) at d=128 take the 16x16x32
+// kernel; at d=64 the 32x32x16 kernel fits four waves per SIMD (the
+// 16x16x32 one needs 142 VGPRs there) and stays faster.
 template <int D, bool DROP, int NREP>
 static void launch_fwd_bf16_m(const FwdArgs& a, dim3 g, hipStream_t s) {
-  if (DROP || a.p.bm || a.p.wl < a.p.N || a.p.wr < a.p.N)
+  if (DROP || a.p.bm || a.p.wl < a.p.N || a.p.wr < a.p.N) {
     hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, true>), g, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, DROP>), g, dim3(256), 0, s, a);
+  } else if constexpr (D == 128) {
+    hipLaunchKernelGGL((fwd_kernel_m16<D, NREP>), g, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, DROP>), g, dim3(256), 0, s, a);
+  }
 }
 
 template <int D>
