@@ -755,6 +755,276 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }  // query blocks of this workgroup
 }
 
+// ------------------------------------------------- dQ, 16x16x32 products
+//
+// The lean dQ pass (no block mask, no window, no dropout) at d=128 on the
+// 16x16x32 matrix instruction (less energy per flop than 32x32x16 under the
+// board's power limit; see the forward's 16x16x32 kernel for the layouts).
+// Per wave two 16-row blocks; per 64-key tile four 16-key blocks:
+//   S^T = K Q^T,  dP^T - D = V dO^T (started at -D),  P = 2^(S c - LSE2),
+//   dS^T = P (dP^T - D),  dQ^T += K^T dS^T   (K^T from transposing reads)
+// Each lane's accumulator registers of a 16x16 block all belong to the
+// lane's query row, so the dP^T chains start at that row's -D directly.
+template <int D>
+struct DqM {
+  static constexpr int BR = 128;  // query rows per workgroup
+  static constexpr int BC = 64;   // keys per tile
+  static constexpr int NKB = BC / 16;
+  static constexpr int NDC = D / 32;
+  static constexpr int NDB = D / 16;
+  using T = SwzTile<D, BC>;
+};
+
+template <int D, int NREP>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel_m16(BwdArgs a) {
+  using C = DqM<D>;
+  using T = typename C::T;
+  __shared__ __attribute__((aligned(1024))) char smem[2][2 * T::BYTES];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int nqb = (p.N + C::BR - 1) / C::BR;
+  static_assert(NREP == 1 || NREP == 2, "one block or a pair");
+  const int nunit = NREP == 2 ? (nqb + 1) / 2 : nqb;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head_lin = L / nunit;
+  const int ui = L - head_lin * nunit;
+  const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
+  const float sl2 = p.scale_l2;
+  const bool causal = p.causal != 0;
+
+  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
+  const int ksb = 2 * (int)a.sk.n, vsb = 2 * (int)a.sv.n;
+  const Rsrc krs = make_rsrc(static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h,
+                             rows_extent(kvalid, ksb, 2 * D));
+  const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
+                             rows_extent(kvalid, vsb, 2 * D));
+  for (int rep = 0; rep < NREP; ++rep) {
+    const int qb = NREP == 2 ? (rep == 0 ? nqb - 1 - ui : ui) : (causal ? nqb - 1 - ui : ui);
+    if (rep == 1) {
+      if (qb == nqb - 1 - ui) break;  // the middle block of an odd count
+      __syncthreads();  // the first block's last tile is no longer read
+    }
+    const int q0 = qb * C::BR;
+    const int r0 = q0 + 32 * w;
+
+    // The lane's rows r0 + li and r0 + 16 + li: Q and dO as B operands
+    // (head-dim chunk dc, slots 8 lg .. 8 lg + 7), and their statistics.
+    bf16x8 qf[2][C::NDC], dof[2][C::NDC];
+    float dneg[2], lse2[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = r0 + 16 * rb + li;
+      const bool ok = row < p.N;
+      const int64_t r = ok ? row : 0;
+      const bf16* Qp = static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h + r * a.sq.n + 8 * lg;
+      const bf16* dOp = static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h + r * a.sdo.n + 8 * lg;
+#pragma unroll
+      for (int dc = 0; dc < C::NDC; ++dc) {
+        qf[rb][dc] = frag_g(Qp + 32 * dc, ok);
+        dof[rb][dc] = frag_g(dOp + 32 * dc, ok);
+      }
+      // D = dO . O over the row (the four lanes of the row hold interleaved
+      // quarters of it), and the LSE in base-2 units (+inf for an empty row);
+      // both stored for the dK/dV kernel.
+      float dpart = 0.f;
+      if (ok) {
+        const int64_t orow = b * a.so.b + h * a.so.h + (int64_t)row * a.so.n + 8 * lg;
+#pragma unroll
+        for (int dc = 0; dc < C::NDC; ++dc) {
+          float o8[8];
+          if (a.o_fp32) {
+            const float* op = static_cast<const float*>(a.o) + orow + 32 * dc;
+            const float4 x0 = *reinterpret_cast<const float4*>(op);
+            const float4 x1 = *reinterpret_cast<const float4*>(op + 4);
+            o8[0] = x0.x; o8[1] = x0.y; o8[2] = x0.z; o8[3] = x0.w;
+            o8[4] = x1.x; o8[5] = x1.y; o8[6] = x1.z; o8[7] = x1.w;
+          } else {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.o) + orow + 32 * dc);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = (float)x[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[rb][dc][e], o8[e], dpart);
+        }
+      }
+      const float dsum = quad_sum(dpart);
+      const int64_t rowstat = ((int64_t)b * p.Hq + h) * p.N + r;
+      lse2[rb] = ok ? lse2_of(a.lse[rowstat]) : kInf;
+      dneg[rb] = -dsum;
+      if (ok && lg == 0) {
+        a.dvec[rowstat] = dsum;
+        a.lse2[rowstat] = lse2[rb];
+      }
+    }
+
+    int kvo[T::NLD], vvo[T::NLD];
+    dma_offsets<D, C::BC>(kvo, ksb, w, lane);
+    dma_offsets<D, C::BC>(vvo, vsb, w, lane);
+    // Row operands (K and V rows 16 kb + li, chunk 4 dc + lg) and K^T
+    // operands (transposing reads: key row 4 lg + e (+ 16, + 32 c) at
+    // head-dim 16 db + 4 a for loader lane 4 e + a), as in the forward.
+    int roff[C::NDC], toff[C::NDB];
+#pragma unroll
+    for (int dc = 0; dc < C::NDC; ++dc) roff[dc] = T::off(li, 4 * dc + lg);
+    {
+      const int rr = 4 * lg + (li >> 2), aa = li & 3;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int d = 16 * db + 4 * aa;
+        toff[db] = rr * T::RB + 16 * ((d >> 3) ^ T::swz(rr)) + 2 * (d & 7);
+      }
+    }
+
+    f32x4 acc[C::NDB][2];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[db][0] = acc[db][1] = f32x4{};
+
+    const int kend = causal ? min(kvalid, q0 + C::BR) : kvalid;
+    const int ntiles = (kend + C::BC - 1) / C::BC;
+    const int64_t log_row =
+        a.log_q ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+    auto issue = [&](int kt, char* stage) {
+      dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
+      dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
+    };
+    int kt = 0;
+    if (kt < ntiles) {
+      issue(kt, smem[0]);
+      wait_dma();
+      __syncthreads();
+    }
+    auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
+      const char* Vs = Ks + T::BYTES;
+      const int key0 = kt * C::BC;
+      const int nxt = kt + 1;
+      if (nxt < ntiles) {
+        paranoid_before_fill();
+        issue(nxt, fill);
+        paranoid_after_fill();
+      }
+      if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
+      const bool need_mask = (causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
+      // Causal pairs: a wave whose rows all lie above the tile's keys has
+      // P = 0 there and skips it (dQ bit-identical).
+      const bool wave_off = NREP == 2 && key0 > r0 + 31;
+      if (!wave_off) {
+        // Two 32-key halves, each S/dP -> P, dS -> dQ products, so that
+        // only half a tile of S and dP is live at once.
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          f32x4 s[2][2], dp[2][2];
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              s[hb][rb] = f32x4{};
+              dp[hb][rb] = f32x4{dneg[rb], dneg[rb], dneg[rb], dneg[rb]};
+            }
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int dc = 0; dc < C::NDC; ++dc)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+              const int kb = 2 * c + hb;
+              const bf16x8 kf = lds_row(Ks + 16 * kb * T::RB, roff[dc]);
+              const bf16x8 vf = lds_row(Vs + 16 * kb * T::RB, roff[dc]);
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb) {
+                s[hb][rb] = mfma16(kf, qf[rb][dc], s[hb][rb]);
+                dp[hb][rb] = mfma16(vf, dof[rb][dc], dp[hb][rb]);
+              }
+            }
+          {
+            // Two reads (K and V) two blocks ahead of their four products.
+            constexpr int NR = C::NDC * 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < NR - 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          }
+          __builtin_amdgcn_s_setprio(0);
+          // P = 2^(S c - LSE2); dS = P (dP - D). Register r of key block
+          // 2 c + hb is key key0 + 32 c + 16 hb + 4 lg + r, of row
+          // r0 + 16 rb + li.
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                s[hb][rb][r] = __builtin_amdgcn_exp2f(fmaf(s[hb][rb][r], sl2, -lse2[rb]));
+          if (__builtin_expect(need_mask, false)) {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int key = key0 + 32 * c + 16 * hb + 4 * lg + r;
+                  const int row = r0 + 16 * rb + li;
+                  const bool kill = (causal && key > row) || key >= kvalid;
+                  s[hb][rb][r] = kill ? 0.f : s[hb][rb][r];
+                }
+          }
+          bf16x8 dsf[2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                dsf[rb][4 * hb + r] = (bf16)(s[hb][rb][r] * dp[hb][rb][r]);
+          __builtin_amdgcn_s_setprio(1);
+          const char* kp = Ks + 32 * c * T::RB;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const bf16x8 ktf = lds_tr(kp, toff[db], toff[db] + 16 * T::RB);
+            acc[db][0] = mfma16(ktf, dsf[0], acc[db][0]);
+            acc[db][1] = mfma16(ktf, dsf[1], acc[db][1]);
+          }
+          {
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < C::NDB - 4; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          }
+          __builtin_amdgcn_s_setprio(0);
+        }
+      }  // !wave_off
+      if (nxt < ntiles) {
+        wait_dma();
+        __syncthreads();
+      }
+      kt = nxt;
+    };
+    for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
+
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = r0 + 16 * rb + li;
+      if (row < p.N) {
+        bf16* dqp = static_cast<bf16*>(a.dq) + b * a.sdq.b + h * a.sdq.h + (int64_t)row * a.sdq.n;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[db][rb][e] * p.scale);
+          *reinterpret_cast<bf16x4*>(dqp + 16 * db + 4 * lg) = v;
+        }
+      }
+    }
+  }  // query blocks of this workgroup
+}
+
 // ----------------------------------------------------------------- launchers
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
@@ -785,6 +1055,10 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef FA_DQ_M16
+#define FA_DQ_M16 1
+#endif
+
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t grid = (int64_t)((a.p.N + 127) / 128) * a.p.Hq * a.p.B;
   const dim3 blk(256);
@@ -805,6 +1079,10 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
   if (head_dim == 64) {
     if (a.p.drop) FA_DQ_LAUNCH(64, true);
     else FA_DQ_LAUNCH(64, false);
+  } else if (!mask && FA_DQ_M16) {
+    // Lean launches at d=128: the 16x16x32 kernel.
+    if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 2>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 1>), g, blk, 0, s, a);
   } else {
     if (a.p.drop) FA_DQ_LAUNCH(128, true);
     else FA_DQ_LAUNCH(128, false);
