@@ -508,6 +508,310 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   }  // key blocks of this workgroup
 }
 
+// ------------------------------------------------- dK, dV, 16x16x32 products
+//
+// The lean dK/dV pass (no block mask, no window, no dropout) at d=128 on the
+// 16x16x32 matrix instruction. Per wave two 16-key blocks (keys
+// k0 + 32 w + 16 kb + i), per step two 16-row query blocks:
+//   S = Q K^T    (A: query rows from the stage, B: the lane's key rows)
+//   dP = dO V^T  (A: dO rows, B: V rows from the workgroup's V block)
+// A lane then holds, for key column i, query rows 4 g .. 4 g + 3 of both
+// query blocks: with block 0 in K slots 0-3 and block 1 in slots 4-7 that
+// is the B operand of
+//   dV^T += dO^T P,   dK^T += Q^T dS   (A: two transposing reads, 4 rows each)
+// the slot order of the forward's P V product. The row statistics of those
+// four rows are one 16-byte LDS read per query block.
+template <int D>
+struct DkdvM {
+  static constexpr int BK = 128;  // keys per workgroup (4 waves x 2 blocks of 16)
+  static constexpr int BQ = 32;   // query rows per step
+  static constexpr int NDC = D / 32;
+  static constexpr int NDB = D / 16;
+  using T = SwzTile<D, BQ>;
+  using VT = SwzTile<D, BK>;
+  // One stage: Q tile | dO tile | LSE log2e of 64 rows | D of 64 rows (the
+  // step's 32 and the next 32, one dword DMA per lane).
+  static constexpr int LSE_OFF = 2 * T::BYTES;
+  static constexpr int DVEC_OFF = LSE_OFF + 256;
+  static constexpr int STAGE = DVEC_OFF + 256;
+  static constexpr int VOFF = 2 * STAGE;
+  static constexpr int LDS_BYTES = VOFF + VT::BYTES;
+  static_assert(STAGE % 256 == 0, "stages keep the 256-byte bank period");
+  static_assert(T::RB == VT::RB, "Q, dO and V rows share lane offsets");
+};
+
+template <int D, int NREP>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
+  using C = DkdvM<D>;
+  using T = typename C::T;
+  using VT = typename C::VT;
+  static_assert(D == 128, "the XOR offset identities below assume 16 chunks per row");
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int nkb = (p.N + C::BK - 1) / C::BK;
+  // Key blocks as in the 32x32 kernel: causal pairs i and nkb - 1 - i.
+  static_assert(NREP == 1 || NREP == 2, "one block or a pair");
+  const int nunit = NREP == 2 ? (nkb + 1) / 2 : nkb;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int head_lin = L / nunit;
+  const int ui = L - head_lin * nunit;
+  const int b = head_lin / p.Hkv, hk = head_lin - b * p.Hkv;
+  const float sl2 = p.scale_l2;
+  const bool causal = p.causal != 0;
+  const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
+  const int qsb = 2 * (int)a.sq.n, dsb = 2 * (int)a.sdo.n, vsb = 2 * (int)a.sv.n;
+
+  for (int rep = 0; rep < NREP; ++rep) {
+    const int kb = rep == 0 ? ui : nkb - 1 - ui;
+    if (rep == 1) {
+      if (kb == ui) break;  // the middle block of an odd count
+      __syncthreads();  // the first block's last step and V block are no longer read
+    }
+    const int k0 = kb * C::BK;
+    const int kw0 = k0 + 32 * w;  // first key of this wave
+    const bf16* Kp = static_cast<const bf16*>(a.k) + b * a.sk.b + hk * a.sk.h;
+    const bf16* Vp = static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h;
+
+    // The lane's keys kw0 + 16 kk + li as B operands (head-dim chunk dc,
+    // slots 8 lg .. 8 lg + 7); keys past the valid length are zero.
+    bf16x8 kf[2][C::NDC];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int key = kw0 + 16 * kk + li;
+      const bool ok = key < kvalid;
+      const bf16* kr = Kp + (int64_t)(ok ? key : 0) * a.sk.n + 8 * lg;
+#pragma unroll
+      for (int dc = 0; dc < C::NDC; ++dc) kf[kk][dc] = frag_g(kr + 32 * dc, ok);
+    }
+    f32x4 dkt[C::NDB][2], dvt[C::NDB][2];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) dkt[db][kk] = dvt[db][kk] = f32x4{};
+
+    if (k0 < kvalid) {  // else every key of the block is masked: dK = dV = 0
+      // Steps: (query head of the group) x (32-row query block), from the
+      // causal diagonal down; query blocks from the last one, heads of the
+      // group innermost.
+      const int qfirst = (causal ? k0 : 0) / C::BQ;
+      const int nq = (p.N + C::BQ - 1) / C::BQ - qfirst;
+      const int nsteps = p.G * nq;
+      auto step_unit = [&](int sidx, int& h, int& q0b) {
+        const int jd = p.G == 1 ? sidx : sidx / p.G;
+        h = hk * p.G + (sidx - jd * p.G);
+        q0b = (qfirst + nq - 1 - jd) * C::BQ;
+      };
+      auto issue = [&](int sidx, char* stage) {
+        int h, q0b;
+        step_unit(sidx, h, q0b);
+        // DMA offsets rebuilt from a fresh lane index (not kept live across
+        // the loop: registers are at their limit).
+        const int ln = fresh_lane_id();
+        int qvo[T::NLD], dvo[T::NLD];
+        dma_offsets<D, C::BQ>(qvo, qsb, w, ln);
+        dma_offsets<D, C::BQ>(dvo, dsb, w, ln);
+        const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
+                                   rows_extent(p.N, qsb, 2 * D));
+        const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
+                                   rows_extent(p.N, dsb, 2 * D));
+        dma_tile<D, C::BQ>(qrs, qvo, (uint32_t)q0b * qsb, stage, w);
+        dma_tile<D, C::BQ>(drs, dvo, (uint32_t)q0b * dsb, stage + T::BYTES, w);
+        if (w < 2) {  // wave-uniform: wave 0 loads LSE, wave 1 D
+          const int64_t row0 = ((int64_t)b * p.Hq + h) * p.N;
+          const Rsrc rs = make_rsrc((w ? a.dvec : a.lse2) + row0, (uint32_t)p.N * 4);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (FA_LDS void*)(stage + (w ? C::DVEC_OFF : C::LSE_OFF)), 4, 4 * ln,
+              (uint32_t)q0b * 4, 0, 0);
+        }
+      };
+      {
+        int vvo[VT::NLD];
+        dma_offsets<D, C::BK>(vvo, vsb, w, lane);
+        const Rsrc vrs = make_rsrc(Vp, rows_extent(kvalid, vsb, 2 * D));
+        dma_tile<D, C::BK>(vrs, vvo, (uint32_t)k0 * vsb, smem + C::VOFF, w);
+      }
+      // Row operands (query, dO and V rows 16 x + li, chunk 4 dc + lg; the
+      // swizzle depends on a row's low 4 bits only, so the 16-row block
+      // base is an immediate) and transposed operands (loader lane 4 e + a
+      // of group lg reads query row 4 lg + e (+ 16) at head-dim 16 db + 4 a).
+      // The swizzle XORs the chunk index, so chunk 4 dc + lg lies at the
+      // dc = 0 offset XOR 64 dc, and head-dim block db at the db = 0 offset
+      // XOR 32 db: one register each stays live, the rest are rebuilt per
+      // step.
+      const int roff0 = T::off(li, lg);
+      int toff0;
+      {
+        const int rr = 4 * lg + (li >> 2), aa = li & 3;
+        const int d = 4 * aa;
+        toff0 = rr * T::RB + 16 * ((d >> 3) ^ T::swz(rr)) + 2 * (d & 7);
+      }
+
+      int sidx = 0;
+      if (sidx < nsteps) issue(sidx, smem);
+      wait_dma();  // the V block and the first step
+      __syncthreads();
+      auto step = [&](const char* __restrict__ Qs, char* __restrict__ fill,
+                      const char* __restrict__ Vb) {
+        const char* dOs = Qs + T::BYTES;
+        int h, q0b;
+        step_unit(sidx, h, q0b);
+        const int nx = sidx + 1;
+        if (nx < nsteps) {  // lands during this step
+          paranoid_before_fill();
+          issue(nx, fill);
+          paranoid_after_fill();
+        }
+        if (a.log_kv && tid == 0)
+          log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
+        const bool need_mask = (causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid);
+        // Causal pairs: when every row of the step lies above the wave's keys
+        // its P is exactly 0 and the step adds nothing to dK or dV.
+        const bool wave_off = NREP == 2 && q0b + C::BQ - 1 < kw0;
+        if (!wave_off) {
+          const char* Vw = Vb + 32 * w * VT::RB;
+          int roff[C::NDC], toff[C::NDB];
+          {
+            int r0 = roff0, t0 = toff0;
+            asm volatile("" : "+v"(r0), "+v"(t0));
+#pragma unroll
+            for (int dc = 0; dc < C::NDC; ++dc) roff[dc] = r0 ^ (64 * dc);
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) toff[db] = t0 ^ (32 * db);
+          }
+          f32x4 s[2][2], dp[2][2];  // [query block][key block]
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) s[rb][kk] = dp[rb][kk] = f32x4{};
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int dc = 0; dc < C::NDC; ++dc) {
+            bf16x8 qa[2], da[2], va[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              qa[x] = lds_row(Qs + 16 * x * T::RB, roff[dc]);
+              da[x] = lds_row(dOs + 16 * x * T::RB, roff[dc]);
+              va[x] = lds_row(Vw + 16 * x * VT::RB, roff[dc]);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) {
+                s[rb][kk] = mfma16(qa[rb], kf[kk][dc], s[rb][kk]);
+                dp[rb][kk] = mfma16(da[rb], va[kk], dp[rb][kk]);
+              }
+          }
+          {
+            // One chunk's six reads ahead of its eight products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+            for (int i = 0; i < C::NDC - 1; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          }
+          __builtin_amdgcn_s_setprio(0);
+          // LSE log2e and D of rows q0b + 16 rb + 4 lg + r, r = 0..3.
+          f32x4 l4[2], d4[2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            l4[rb] = *reinterpret_cast<const f32x4*>(Qs + C::LSE_OFF + 4 * (16 * rb + 4 * lg));
+            d4[rb] = *reinterpret_cast<const f32x4*>(Qs + C::DVEC_OFF + 4 * (16 * rb + 4 * lg));
+          }
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                s[rb][kk][r] = __builtin_amdgcn_exp2f(fmaf(s[rb][kk][r], sl2, -l4[rb][r]));
+          if (__builtin_expect(need_mask, false)) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int key = kw0 + 16 * kk + li;
+                  const int row = q0b + 16 * rb + 4 * lg + r;
+                  const bool kill = (causal && key > row) || key >= kvalid;
+                  s[rb][kk][r] = kill ? 0.f : s[rb][kk][r];
+                }
+          }
+          bf16x8 pf[2], dsf[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                pf[kk][4 * rb + r] = (bf16)s[rb][kk][r];
+                dsf[kk][4 * rb + r] = (bf16)(s[rb][kk][r] * (dp[rb][kk][r] - d4[rb][r]));
+              }
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const bf16x8 dot = lds_tr(dOs, toff[db], toff[db] + 16 * T::RB);
+            const bf16x8 qt = lds_tr(Qs, toff[db], toff[db] + 16 * T::RB);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              dvt[db][kk] = mfma16(dot, pf[kk], dvt[db][kk]);
+              dkt[db][kk] = mfma16(qt, dsf[kk], dkt[db][kk]);
+            }
+          }
+          {
+            // Two head-dim blocks of reads ahead of their products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < C::NDB - 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          }
+          __builtin_amdgcn_s_setprio(0);
+        }  // !wave_off
+        if (nx < nsteps) {
+          wait_dma();
+          __syncthreads();
+        }
+        sidx = nx;
+      };
+      for (int st = 0; sidx < nsteps; st ^= 1)
+        step(smem + st * C::STAGE, smem + (st ^ 1) * C::STAGE, smem + C::VOFF);
+    }
+
+    // Register e of block (db, kk) is head-dim 16 db + 4 lg + e of key
+    // kw0 + 16 kk + li.
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int key = kw0 + 16 * kk + li;
+      if (key < p.N) {
+        bf16* dkp = static_cast<bf16*>(a.dk) + b * a.sdk.b + hk * a.sdk.h + (int64_t)key * a.sdk.n;
+        bf16* dvp = static_cast<bf16*>(a.dv) + b * a.sdv.b + hk * a.sdv.h + (int64_t)key * a.sdv.n;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          bf16x4 kq, vq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kq[e] = (bf16)(dkt[db][kk][e] * p.scale);
+            vq[e] = (bf16)dvt[db][kk][e];
+          }
+          *reinterpret_cast<bf16x4*>(dkp + 16 * db + 4 * lg) = kq;
+          *reinterpret_cast<bf16x4*>(dvp + 16 * db + 4 * lg) = vq;
+        }
+      }
+    }
+  }  // key blocks of this workgroup
+}
+
 // ----------------------------------------------------------------- dQ
 
 template <int D>
@@ -1027,6 +1331,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel_m16(BwdArgs a) {
 
 // ----------------------------------------------------------------- launchers
 
+#ifndef FA_DKDV_M16
+#define FA_DKDV_M16 1
+#endif
+
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t nkb = (a.p.N + 127) / 128;
   const dim3 blk(256);
@@ -1047,6 +1355,10 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   if (head_dim == 64) {
     if (a.p.drop) FA_DKDV_LAUNCH(64, true);
     else FA_DKDV_LAUNCH(64, false);
+  } else if (!mask && FA_DKDV_M16) {
+    // Lean launches at d=128: the 16x16x32 kernel.
+    if (pair) hipLaunchKernelGGL((bwd_dkdv_kernel_m16<128, 2>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel_m16<128, 1>), g, blk, 0, s, a);
   } else {
     if (a.p.drop) FA_DKDV_LAUNCH(128, true);
     else FA_DKDV_LAUNCH(128, false);
