@@ -61,16 +61,26 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// All-reduce over the four lanes i, i + 16, i + 32, i + 48 (one column of
-// a 16x16 result): v_permlane16_swap pairs lanes 16 apart,
-// v_permlane32_swap lanes 32 apart; applied to (x, x) each returns x of
-// the lane and of its partner, in some order.
-__device__ __forceinline__ float quad_max(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+// All-reduces over the four lanes i, i + 16, i + 32, i + 48 (one column
+// of a 16x16 result). v_permlane16_swap exchanges the odd 16-lane groups of
+// its first operand with the even groups of its second, v_permlane32_swap
+// the upper half of the first with the lower half of the second.
+//
+// Maximum of a and of b at once: the 16-lane swap of (a, b) leaves a's
+// pair maxima in lane groups 0 and 2 and b's in groups 1 and 3, the
+// 32-lane swap completes both, and a last 16-lane swap of that result with
+// itself returns a's maximum in its first output and b's in its second.
+__device__ __forceinline__ void quad_max2(float a, float b, float& ma, float& mb) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  float x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  ma = __uint_as_float(r[0]);
+  mb = __uint_as_float(r[1]);
 }
+// Sum: each swap applied to (x, x) returns x of the lane and of its
+// partner, in some order.
 __device__ __forceinline__ float quad_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(r[0]) + __uint_as_float(r[1]);

@@ -681,15 +681,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
                 s[kb][rb][r] = kill ? -kInf : s[kb][rb][r];
               }
         }
+        // Row maxima: a chain of three-input maxima over the lane's 16 values
+        // of each row, then one lane exchange for both rows.
         float mx[2];
+        {
+          float m2[2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          float m4 = fmaxf(fmaxf(s[0][rb][0], s[0][rb][1]), fmaxf(s[0][rb][2], s[0][rb][3]));
+          for (int rb = 0; rb < 2; ++rb) {
+            float m = fmaxf(s[0][rb][0], s[0][rb][1]);
 #pragma unroll
-          for (int kb = 1; kb < C::NKB; ++kb)
-            m4 = fmaxf(m4, fmaxf(fmaxf(s[kb][rb][0], s[kb][rb][1]),
-                                 fmaxf(s[kb][rb][2], s[kb][rb][3])));
-          mx[rb] = quad_max(m4) * sl2;
+            for (int k = 2; k < 4 * C::NKB; k += 2)
+              m = fmaxf(fmaxf(m, s[k >> 2][rb][k & 3]), s[(k + 1) >> 2][rb][(k + 1) & 3]);
+            m2[rb] = m;
+          }
+          quad_max2(m2[0], m2[1], mx[0], mx[1]);
+          mx[0] *= sl2;
+          mx[1] *= sl2;
         }
         if (wave_any(mx[0] > m_ref[0] + C::kLag || mx[1] > m_ref[1] + C::kLag)) {
 #pragma unroll
