@@ -117,15 +117,14 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Pairwise (tree) reductions of one accumulator block: 15 operations in a
-// dependency chain of depth 4 instead of 15.
+// Tree reductions of one accumulator block. The maximum uses three-input
+// maxima (v_max3_f32): 8 operations in a dependency chain of depth 3; the
+// sum is pairwise: 15 operations, depth 4 instead of 15.
 __device__ __forceinline__ float tree_max16(const f32x16& s) {
-  float a[8];
+  float a[5];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = fmaxf(s[i], s[i + 8]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = fmaxf(a[i], a[i + 4]);
-  return fmaxf(fmaxf(a[0], a[2]), fmaxf(a[1], a[3]));
+  for (int i = 0; i < 5; ++i) a[i] = fmaxf(fmaxf(s[3 * i], s[3 * i + 1]), s[3 * i + 2]);
+  return fmaxf(fmaxf(fmaxf(a[0], a[1]), a[2]), fmaxf(fmaxf(a[3], a[4]), s[15]));
 }
 __device__ __forceinline__ float tree_sum16(const f32x16& s) {
   float a[8];
