@@ -64,7 +64,58 @@ def parse_args():
     ap.add_argument("--io-sweep", action="store_true",
                     help="instead of the benchmark: forward + backward at N = 1K .. 16K, d = 128, "
                          "B * H * N fixed, one JSON line per N with the three byte models")
+    ap.add_argument("--mix-ceiling", action="store_true",
+                    help="instead of the benchmark: time the instruction-mix grid of "
+                         "libfa_mixbench.so (64 matrix products per wave-tile with E "
+                         "exponentials and F other VALU operations, two waves per SIMD); one "
+                         "JSON line per mix")
     return ap.parse_args()
+
+
+MIX_ITERS = 1024     # wave-tiles per wave in one timed launch
+MIX_REPS = 3         # timed launches per mix (the best one counts)
+MIX_WAVES = 512 * 4  # 512 workgroups of four waves: two per SIMD on 256 CUs
+
+
+def mix_ceiling():
+    """Time every mix of the measurement library's grid and print one JSON
+    line each: nanoseconds per wave-tile per SIMD (two waves share a SIMD)
+    and the matrix-product rate that mix allows."""
+    import ctypes
+
+    path = os.path.join(ROOT, "exact_io_aware_29_amd", "libfa_mixbench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_29_amd.build`")
+    lib = ctypes.CDLL(path)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.fa_mixbench_grid.restype = ctypes.c_int
+    lib.fa_mixbench_grid.argtypes = [ip, ip, ip, ip, ip]
+    lib.fa_mixbench.restype = ctypes.c_int
+    lib.fa_mixbench.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_float)]
+    ne, nf, nl = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rows, trs = (ctypes.c_int * 8)(), (ctypes.c_int * 8)()
+    lib.fa_mixbench_grid(ctypes.byref(ne), ctypes.byref(nf), ctypes.byref(nl), rows, trs)
+    # About a second of the heaviest mix first, so that every timed mix runs
+    # at the board's settled clock and power (the first launches of a fresh
+    # process otherwise run while the clock is still moving).
+    ms = ctypes.c_float()
+    rc = lib.fa_mixbench(ne.value - 1, nf.value - 1, nl.value - 1, 4 * MIX_ITERS, 200,
+                         ctypes.byref(ms))
+    if rc != 0:
+        raise RuntimeError(f"fa_mixbench warm-up failed with code {rc}")
+    flops = MIX_WAVES * MIX_ITERS * 64 * 2 * 16 * 16 * 32
+    for li in range(nl.value):
+        for ei in range(ne.value):
+            for fi in range(nf.value):
+                rc = lib.fa_mixbench(ei, fi, li, MIX_ITERS, MIX_REPS, ctypes.byref(ms))
+                if rc != 0:
+                    raise RuntimeError(f"fa_mixbench({ei}, {fi}, {li}) failed with code {rc}")
+                print(json.dumps({
+                    "mix_ceiling": True, "mfma_per_tile": 64, "exp_per_tile": 8 * ei,
+                    "valu_per_tile": 32 * fi, "lds_row_reads": rows[li], "lds_tr_reads": trs[li],
+                    "ms": round(ms.value, 4),
+                    "ns_per_wave_tile_per_simd": round(ms.value * 1e6 / (2 * MIX_ITERS), 1),
+                    "tflops": round(flops / (ms.value * 1e-3) / 1e12, 1)}), flush=True)
 
 
 def source_hash(kernel: str) -> str:
@@ -388,6 +439,10 @@ def main():
               "(batch, head) with no communication, so one GPU's figure is the per-GPU rate.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.mix_ceiling:
+        mix_ceiling()
+        return
 
     import numpy as np
     import torch

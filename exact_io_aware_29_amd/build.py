@@ -48,8 +48,23 @@ PARANOID_OUT = os.path.join(PKG, "libfa_paranoid.so")
 PARANOID_FLAGS = ["-DFA_PARANOID_BARRIERS=1"]
 
 
+# Measurement only: the instruction-mix ceiling of the matrix-core kernels
+# (a grid of products / exponentials / other VALU mixes, timed by
+# ``bench.py --mix-ceiling``). The attention library does not load it.
+MIXBENCH_SRC = "mixbench.hip"
+MIXBENCH_OUT = os.path.join(PKG, "libfa_mixbench.so")
+
+
 def _compile(job) -> str:
     src, variant = job
+    if variant == "mixbench":
+        tmp = MIXBENCH_OUT + ".tmp"
+        cmd = [HIPCC, *FLAGS, "-shared", "-x", "hip", os.path.join(CSRC, src), "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, MIXBENCH_OUT)
+        return MIXBENCH_OUT
     objdir = os.path.join(OBJDIR, variant) if variant else OBJDIR
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip", *KERNEL_FLAGS] if src.endswith(".hip") else []
@@ -103,18 +118,20 @@ def build_sanitized(verbose: bool = False):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libfa.so`` and the debug variant
-    ``libfa_paranoid.so``; returns the path of ``libfa.so``."""
+    """Compile every source and link ``libfa.so``, the debug variant
+    ``libfa_paranoid.so`` and the measurement library
+    ``libfa_mixbench.so``; returns the path of ``libfa.so``."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(os.path.join(OBJDIR, "paranoid"), exist_ok=True)
-    jobs = [(s, "") for s in SOURCES] + [(s, "paranoid") for s in SOURCES]
+    jobs = ([(s, "") for s in SOURCES] + [(s, "paranoid") for s in SOURCES] +
+            [(MIXBENCH_SRC, "mixbench")])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         objs = list(ex.map(_compile, jobs))
     _link(objs[:len(SOURCES)], OUT)
-    _link(objs[len(SOURCES):], PARANOID_OUT)
+    _link(objs[len(SOURCES):2 * len(SOURCES)], PARANOID_OUT)
     if verbose:
-        print(f"built {OUT} and {PARANOID_OUT}")
+        print(f"built {OUT}, {PARANOID_OUT} and {MIXBENCH_OUT}")
     build_sanitized(verbose)
     return OUT
 

@@ -77,3 +77,25 @@ def test_recorded_traffic_lines_parse():
             assert got == (int(nbytes) if src == bench.source_hash(kernel) else None)
             found += 1
     assert found > 0
+
+
+def test_mixbench_library_exports_its_entry_points():
+    """The instruction-mix measurement library is built beside libfa.so and
+    exports the grid query and the timing call (no GPU call made here)."""
+    import ctypes
+
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "exact_io_aware_29_amd", "libfa_mixbench.so")
+    assert os.path.exists(path), "build first: python -m exact_io_aware_29_amd.build"
+    lib = ctypes.CDLL(path)
+    ne, nf, nl = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rows, trs = (ctypes.c_int * 3)(), (ctypes.c_int * 3)()
+    assert lib.fa_mixbench_grid(ctypes.byref(ne), ctypes.byref(nf), ctypes.byref(nl), rows, trs) == 0
+    assert (ne.value, nf.value, nl.value) == (5, 6, 3)
+    assert list(rows) == [0, 16, 24] and list(trs) == [0, 32, 32]
+    ms = ctypes.c_float()
+    # an index outside the grid or a bad count is refused before any HIP call
+    assert lib.fa_mixbench(5, 0, 0, 1, 1, ctypes.byref(ms)) == -1
+    assert lib.fa_mixbench(0, -1, 0, 1, 1, ctypes.byref(ms)) == -1
+    assert lib.fa_mixbench(0, 0, 3, 1, 1, ctypes.byref(ms)) == -1
+    assert lib.fa_mixbench(0, 0, 0, 0, 1, ctypes.byref(ms)) == -1
