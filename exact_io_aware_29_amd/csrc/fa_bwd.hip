@@ -527,8 +527,8 @@ struct DkdvM {
   static constexpr int BQ = 32;   // query rows per step
   static constexpr int NDC = D / 32;
   static constexpr int NDB = D / 16;
-  using T = SwzTile<D, BQ>;
-  using VT = SwzTile<D, BK>;
+  using T = SwzTile<D, BQ, 1>;
+  using VT = SwzTile<D, BK, 1>;
   // One stage: Q tile | dO tile | LSE log2e of 64 rows | D of 64 rows (the
   // step's 32 and the next 32, one dword DMA per lane).
   static constexpr int LSE_OFF = 2 * T::BYTES;
@@ -612,8 +612,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
         // the loop: registers are at their limit).
         const int ln = fresh_lane_id();
         int qvo[T::NLD], dvo[T::NLD];
-        dma_offsets<D, C::BQ>(qvo, qsb, w, ln);
-        dma_offsets<D, C::BQ>(dvo, dsb, w, ln);
+        dma_offsets_t<T>(qvo, qsb, w, ln);
+        dma_offsets_t<T>(dvo, dsb, w, ln);
         const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
                                    rows_extent(p.N, qsb, 2 * D));
         const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
       };
       {
         int vvo[VT::NLD];
-        dma_offsets<D, C::BK>(vvo, vsb, w, lane);
+        dma_offsets_t<VT>(vvo, vsb, w, lane);
         const Rsrc vrs = make_rsrc(Vp, rows_extent(kvalid, vsb, 2 * D));
         dma_tile<D, C::BK>(vrs, vvo, (uint32_t)k0 * vsb, smem + C::VOFF, w);
       }
@@ -1076,7 +1076,7 @@ struct DqM {
   static constexpr int NKB = BC / 16;
   static constexpr int NDC = D / 32;
   static constexpr int NDB = D / 16;
-  using T = SwzTile<D, BC>;
+  using T = SwzTile<D, BC, 1>;
 };
 
 template <int D, int NREP>
@@ -1165,8 +1165,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel_m16(BwdArgs a) {
     }
 
     int kvo[T::NLD], vvo[T::NLD];
-    dma_offsets<D, C::BC>(kvo, ksb, w, lane);
-    dma_offsets<D, C::BC>(vvo, vsb, w, lane);
+    dma_offsets_t<T>(kvo, ksb, w, lane);
+    dma_offsets_t<T>(vvo, vsb, w, lane);
     // Row operands (K and V rows 16 kb + li, chunk 4 dc + lg) and K^T
     // operands (transposing reads: key row 4 lg + e (+ 16, + 32 c) at
     // head-dim 16 db + 4 a for loader lane 4 e + a), as in the forward.

@@ -532,7 +532,7 @@ struct FwdM {
   static constexpr int NKB = BC / 16;
   static constexpr int NDC = D / 32;  // 32-wide head-dim chunks of the S products
   static constexpr int NDB = D / 16;  // 16-wide head-dim blocks of O^T
-  using T = SwzTile<D, BC>;
+  using T = SwzTile<D, BC, 1>;
   static constexpr float kLag = 8.f;
 };
 
@@ -587,8 +587,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
       for (int dc = 0; dc < C::NDC; ++dc) qf[rb][dc] = frag_g(qrow + 32 * dc, ok);
     }
     int kvo[T::NLD], vvo[T::NLD];
-    dma_offsets<D, C::BC>(kvo, ksb, w, lane);
-    dma_offsets<D, C::BC>(vvo, vsb, w, lane);
+    dma_offsets_t<T>(kvo, ksb, w, lane);
+    dma_offsets_t<T>(vvo, vsb, w, lane);
     // K operand of key block kb, chunk dc: key row 16 kb + li, 16-byte chunk
     // 4 dc + lg; the swizzle depends on the row's low 4 bits only, so block
     // kb adds 16 kb rows as an immediate.

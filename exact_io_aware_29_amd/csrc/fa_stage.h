@@ -146,7 +146,21 @@ __device__ __forceinline__ uint32_t rows_extent(int rows, int sb, int rb) {
   return rows > 0 ? (uint32_t)(rows - 1) * (uint32_t)sb + (uint32_t)rb : 0u;
 }
 
-template <int D, int ROWS>
+// SW selects the chunk swizzle by the reads that the tile serves. LDS has
+// 64 banks of 4 bytes; the lanes served in one cycle must hit distinct
+// banks. Measured on gfx950 (bank-conflict counters over 68 candidate
+// swizzles): a 16-byte read serves together the 16 lanes with equal lane
+// bit 5 and equal parity of lane bits 2..4; an 8-byte transposing read
+// serves each 32-lane half together.
+//   SW = 0, the 32x32 products' reads (rows in swap_bits23 order, chunk
+//           pairs per lane half; transposing reads of 4-row groups);
+//   SW = 1, the 16x16x32 products (d = 128): row reads of 16 rows x 4
+//           consecutive chunks (lane i + 16 g: row i, chunk 4 c + g) and
+//           transposing reads of 8 rows x a chunk pair (2 k, 2 k + 1).
+//           For an XOR swizzle S both are conflict-free iff S^-1(1) has
+//           bits 2 and 3 set; this S maps row 12 to 1.
+// Either swizzle depends on a row's low 4 bits only.
+template <int D, int ROWS, int SW = 0>
 struct SwzTile {
   static constexpr int RB = 2 * D;            // bytes per row
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
@@ -154,11 +168,11 @@ struct SwzTile {
   static constexpr int NLD = BYTES / (256 * 16);  // DMA loads per thread
   static_assert(BYTES % (256 * 16) == 0, "tile must be a whole number of workgroup loads");
   static_assert(ROWS % 16 == 0, "operand fetch works on 16-row groups");
-  // Chunk swizzle: a bijection on the row's chunk index chosen so that 16
-  // consecutive rows at one chunk, and 4 consecutive rows x 4 consecutive
-  // chunks, each spread over all 64 banks.
+  static_assert(SW == 0 || D == 128, "the 16x16x32 swizzle is for 16 chunks per row");
   __device__ static __forceinline__ int swz(int r) {
-    if constexpr (D == 64) {
+    if constexpr (SW == 1) {
+      return (((r & 7) << 1) | ((r >> 3) & 1)) ^ (r & 8);
+    } else if constexpr (D == 64) {
       return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
     } else {
       return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -168,11 +182,11 @@ struct SwzTile {
 };
 
 // Per-lane global byte offsets (relative to the tile's first row) of the
-// DMA loads that fill one tile when NW waves share the work; computed once
-// per kernel. Wave w's load i fills LDS kibibyte i * NW + w of the tile.
-template <int D, int ROWS, int NL, int NW = 4>
-__device__ __forceinline__ void dma_offsets(int (&voff)[NL], int stride_bytes, int w, int lane) {
-  using T = SwzTile<D, ROWS>;
+// DMA loads that fill one tile of type T when NW waves share the work;
+// computed once per kernel. Wave w's load i fills LDS kibibyte i * NW + w
+// of the tile.
+template <class T, int NL, int NW = 4>
+__device__ __forceinline__ void dma_offsets_t(int (&voff)[NL], int stride_bytes, int w, int lane) {
   static_assert(NL * NW * 1024 == T::BYTES, "one offset per DMA load");
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
@@ -180,6 +194,11 @@ __device__ __forceinline__ void dma_offsets(int (&voff)[NL], int stride_bytes, i
     const int r = p / T::CPR, pc = p % T::CPR;
     voff[i] = (int)((uint32_t)r * (uint32_t)stride_bytes + 16u * (uint32_t)(pc ^ T::swz(r)));
   }
+}
+
+template <int D, int ROWS, int NL, int NW = 4>
+__device__ __forceinline__ void dma_offsets(int (&voff)[NL], int stride_bytes, int w, int lane) {
+  dma_offsets_t<SwzTile<D, ROWS>, NL, NW>(voff, stride_bytes, w, lane);
 }
 
 template <int D, int ROWS, int NW = 4>
