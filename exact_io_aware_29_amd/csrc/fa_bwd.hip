@@ -1370,6 +1370,9 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
 #ifndef FA_DQ_M16
 #define FA_DQ_M16 1
 #endif
+#ifndef FA_DQ_M16_D64
+#define FA_DQ_M16_D64 1
+#endif
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t grid = (int64_t)((a.p.N + 127) / 128) * a.p.Hq * a.p.B;
@@ -1388,13 +1391,18 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
       else hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 1, DR>), g, blk, 0, s, a);       \
     }                                                                                    \
   } while (0)
-  if (head_dim == 64) {
+  if (!mask && FA_DQ_M16 && (head_dim == 128 || FA_DQ_M16_D64)) {
+    // Lean launches: the 16x16x32 kernel.
+    if (head_dim == 64) {
+      if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<64, 2>), g, blk, 0, s, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel_m16<64, 1>), g, blk, 0, s, a);
+    } else {
+      if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 2>), g, blk, 0, s, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 1>), g, blk, 0, s, a);
+    }
+  } else if (head_dim == 64) {
     if (a.p.drop) FA_DQ_LAUNCH(64, true);
     else FA_DQ_LAUNCH(64, false);
-  } else if (!mask && FA_DQ_M16) {
-    // Lean launches at d=128: the 16x16x32 kernel.
-    if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 2>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 1>), g, blk, 0, s, a);
   } else {
     if (a.p.drop) FA_DQ_LAUNCH(128, true);
     else FA_DQ_LAUNCH(128, false);

@@ -154,11 +154,13 @@ __device__ __forceinline__ uint32_t rows_extent(int rows, int sb, int rb) {
 // serves each 32-lane half together.
 //   SW = 0, the 32x32 products' reads (rows in swap_bits23 order, chunk
 //           pairs per lane half; transposing reads of 4-row groups);
-//   SW = 1, the 16x16x32 products (d = 128): row reads of 16 rows x 4
-//           consecutive chunks (lane i + 16 g: row i, chunk 4 c + g) and
-//           transposing reads of 8 rows x a chunk pair (2 k, 2 k + 1).
-//           For an XOR swizzle S both are conflict-free iff S^-1(1) has
-//           bits 2 and 3 set; this S maps row 12 to 1.
+//   SW = 1, the 16x16x32 products: row reads of 16 rows x 4 consecutive
+//           chunks (lane i + 16 g: row i, chunk 4 c + g) and transposing
+//           reads of 8 rows x a chunk pair (2 k, 2 k + 1). At d = 128, an
+//           XOR swizzle S makes both conflict-free iff S^-1(1) has bits 2
+//           and 3 set; this S maps row 12 to 1. At d = 64 (two rows per
+//           bank period, row bit 0 picks the bank half) S(r) = r AND 6
+//           does.
 // Either swizzle depends on a row's low 4 bits only.
 template <int D, int ROWS, int SW = 0>
 struct SwzTile {
@@ -168,9 +170,11 @@ struct SwzTile {
   static constexpr int NLD = BYTES / (256 * 16);  // DMA loads per thread
   static_assert(BYTES % (256 * 16) == 0, "tile must be a whole number of workgroup loads");
   static_assert(ROWS % 16 == 0, "operand fetch works on 16-row groups");
-  static_assert(SW == 0 || D == 128, "the 16x16x32 swizzle is for 16 chunks per row");
+  static_assert(SW == 0 || D == 128 || D == 64, "16x16x32 swizzles for d = 64 and 128");
   __device__ static __forceinline__ int swz(int r) {
-    if constexpr (SW == 1) {
+    if constexpr (SW == 1 && D == 64) {
+      return r & 6;
+    } else if constexpr (SW == 1) {
       return (((r & 7) << 1) | ((r >> 3) & 1)) ^ (r & 8);
     } else if constexpr (D == 64) {
       return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
