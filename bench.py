@@ -50,13 +50,13 @@ def parse_args():
                     help="workload id (2 = the headline B64 H16 N1024 d64 shape; 7 = decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
-    ap.add_argument("--no-north-star", action="store_true",
-                    help="with the default workload, skip the north_star_c3 record (the causal "
+    ap.add_argument("--no-w3-record", action="store_true",
+                    help="with the default workload, skip the w3_record field (the causal "
                          "key-padded B8 H16 N4096 d128 workload measured in the same run)")
-    ap.add_argument("--c3-steps", type=int, default=20,
-                    help="timed steps of the north_star_c3 measurement")
-    ap.add_argument("--c3-warmup", type=int, default=5,
-                    help="untimed warmup steps of the north_star_c3 measurement")
+    ap.add_argument("--w3-steps", type=int, default=20,
+                    help="timed steps of the w3_record measurement")
+    ap.add_argument("--w3-warmup", type=int, default=5,
+                    help="untimed warmup steps of the w3_record measurement")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -465,18 +465,18 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(inp, per_b, args.cpu_seconds)
     rec.pop("_per_b", None)
     del inp
-    if args.workload == 2 and not args.no_north_star:
-        rec["north_star_c3"] = north_star_c3(args, dev)
+    if args.workload == 2 and not args.no_w3_record:
+        rec["w3_record"] = w3_record(args, dev)
     print(json.dumps(rec), flush=True)
 
 
 # Targets of the causal key-padded B8 H16 N4096 d128 configuration: the
 # forward at >= 50 % and forward + backward at >= 35 % of the bf16 dense
 # matrix-core peak.
-C3_TARGET_PCT = {"fwd": 50.0, "fwd_bwd": 35.0}
+W3_TARGET_PCT = {"fwd": 50.0, "fwd_bwd": 35.0}
 
 
-def north_star_c3(args, dev):
+def w3_record(args, dev):
     """The causal, key-padded B8 H16 N4096 d128 bf16 workload (workload 3),
     measured in the same run as the headline line: forward and
     forward + backward time, TFLOP/s and % of the bf16 peak, each kernel's
@@ -485,7 +485,7 @@ def north_star_c3(args, dev):
 
     w = WORKLOADS[3]
     inp = draw(w, 3)
-    r = measure(args, 3, w, inp, dev, args.c3_steps, args.c3_warmup)
+    r = measure(args, 3, w, inp, dev, args.w3_steps, args.w3_warmup)
     del inp
     k = r["kernels"]
     fwd_ms = k["fwd"]["ms"]
@@ -495,7 +495,7 @@ def north_star_c3(args, dev):
     fb_pct = 100 * fb_tf / k["fwd"]["peak"]
     return {
         "workload": r["config"]["workload"],
-        "steps": args.c3_steps, "warmup": args.c3_warmup,
+        "steps": args.w3_steps, "warmup": args.w3_warmup,
         "fwd_ms": round(fwd_ms, 4),
         "fwd_tflops": r["fwd_tflops"],
         "pct_of_peak_fwd": round(fwd_pct, 2),
@@ -507,9 +507,9 @@ def north_star_c3(args, dev):
                     for n, v in k.items()},
         "dominant_kernel": r["roofline"]["kernel"],
         "dominant_frac": r["roofline"]["frac"],
-        "target_pct": C3_TARGET_PCT,
-        "target_met": {"fwd": fwd_pct >= C3_TARGET_PCT["fwd"],
-                       "fwd_bwd": fb_pct >= C3_TARGET_PCT["fwd_bwd"]},
+        "target_pct": W3_TARGET_PCT,
+        "target_met": {"fwd": fwd_pct >= W3_TARGET_PCT["fwd"],
+                       "fwd_bwd": fb_pct >= W3_TARGET_PCT["fwd_bwd"]},
     }
 
 
