@@ -64,6 +64,10 @@ def parse_args():
     ap.add_argument("--io-sweep", action="store_true",
                     help="instead of the benchmark: forward + backward at N = 1K .. 16K, d = 128, "
                          "B * H * N fixed, one JSON line per N with the three byte models")
+    ap.add_argument("--fill", choices=("random", "zeros", "half"), default="random",
+                    help="power analysis only: overwrite Q, K, V and dO with zeros or 0.5 "
+                         "(same shapes, masks and kernels; the data field says so). The clock "
+                         "follows board power, so timing depends on the data")
     ap.add_argument("--mix-ceiling", action="store_true",
                     help="instead of the benchmark: time the instruction-mix grid of "
                          "libfa_mixbench.so (64 matrix products per wave-tile with E "
@@ -532,6 +536,9 @@ def measure(args, workload_id, w, inp, dev, steps, warmup):
 
     q, k, v = t(inp.q), t(inp.k), t(inp.v)
     do = t(inp.do) if w.backward else None
+    if args.fill != "random" and w.dtype != "fp8":
+        for x in (q, k, v) + ((do,) if do is not None else ()):
+            x.fill_(0.0 if args.fill == "zeros" else 0.5)
     sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).to(dev)
     bm = None if inp.block_mask is None else torch.from_numpy(inp.block_mask).to(dev)
     kw = dict(scale=inp.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, window=w.window)
@@ -634,7 +641,10 @@ def measure(args, workload_id, w, inp, dev, steps, warmup):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": ("synthetic (seeded N(0,1) inputs, encoded as e4m3 of x / descale)"
-                 if w.dtype == "fp8" else "synthetic (seeded N(0,1) inputs, rounded to bf16)"),
+                 if w.dtype == "fp8" else
+                 "synthetic (seeded N(0,1) inputs, rounded to bf16)" if args.fill == "random" else
+                 f"synthetic, every input element {'0' if args.fill == 'zeros' else '0.5'} "
+                 "(power analysis, not a benchmark value)"),
         "config": {"workload": w.describe(), "batch": w.batch, "heads_q": w.heads_q,
                    "heads_kv": w.heads_kv, "seqlen": w.seqlen, "head_dim": w.head_dim,
                    "causal": w.causal, "pass": "fwd+bwd" if w.backward else "fwd",
