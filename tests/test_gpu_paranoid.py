@@ -42,6 +42,8 @@ CASES = [
     (1, 4, 2, 520, 128, True, None, None, (100, 0), 0.0),      # sliding window
     (2, 2, 1, 300, 64, True, [300, 77], None, None, 0.2),      # dropout
     (1, 2, 2, 700, 128, False, "random", "butterfly", None, 0.0),
+    (1, 2, 2, 333, 128, False, "random", None, None, 0.0),    # lean one-block, d=128
+    (1, 4, 2, 520, 64, True, None, None, None, 0.0),           # lean causal pairs, d=64
 ]
 
 
