@@ -521,16 +521,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 //   dV^T += dO^T P,   dK^T += Q^T dS   (A: two transposing reads, 4 rows each)
 // the slot order of the forward's P V product. The row statistics of those
 // four rows are one 16-byte LDS read per query block.
-template <int D>
+template <int D, int NW>
 struct DkdvM {
-  static constexpr int BK = 128;  // keys per workgroup (4 waves x 2 blocks of 16)
-  static constexpr int BQ = 32;   // query rows per step
+  // Keys per workgroup: NW waves x 2 blocks of 16. Query rows per step: 32
+  // with 4 waves (two workgroups per CU hold two stages and the V block);
+  // 64 with 8 waves (one workgroup per CU, still two waves per SIMD), as two
+  // 32-row sub-blocks per barrier, which halves the barriers and the Q / dO
+  // DMA per product.
+  static constexpr int BK = 32 * NW;
+  static constexpr int BQ = NW == 8 ? 64 : 32;
+  static constexpr int NSB = BQ / 32;
   static constexpr int NDC = D / 32;
   static constexpr int NDB = D / 16;
   using T = SwzTile<D, BQ, 1>;
   using VT = SwzTile<D, BK, 1>;
-  // One stage: Q tile | dO tile | LSE log2e of 64 rows | D of 64 rows (the
-  // step's 32 and the next 32, one dword DMA per lane).
+  static constexpr int QNL = T::BYTES / (NW * 1024);   // DMA loads per thread, Q or dO tile
+  static constexpr int VNL = VT::BYTES / (NW * 1024);  // DMA loads per thread, V block
+  // One stage: Q tile | dO tile | LSE log2e of 64 rows | D of 64 rows (one
+  // dword DMA per lane; at BQ = 32 the next step's 32 rows come along).
   static constexpr int LSE_OFF = 2 * T::BYTES;
   static constexpr int DVEC_OFF = LSE_OFF + 256;
   static constexpr int STAGE = DVEC_OFF + 256;
@@ -540,9 +548,9 @@ struct DkdvM {
   static_assert(T::RB == VT::RB, "Q, dO and V rows share lane offsets");
 };
 
-template <int D, int NREP>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
-  using C = DkdvM<D>;
+template <int D, int NREP, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
+  using C = DkdvM<D, NW>;
   using T = typename C::T;
   using VT = typename C::VT;
   static_assert(D == 128, "the XOR offset identities below assume 16 chunks per row");
@@ -611,15 +619,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
         // DMA offsets rebuilt from a fresh lane index (not kept live across
         // the loop: registers are at their limit).
         const int ln = fresh_lane_id();
-        int qvo[T::NLD], dvo[T::NLD];
-        dma_offsets_t<T>(qvo, qsb, w, ln);
-        dma_offsets_t<T>(dvo, dsb, w, ln);
+        int qvo[C::QNL], dvo[C::QNL];
+        dma_offsets_t<T, C::QNL, NW>(qvo, qsb, w, ln);
+        dma_offsets_t<T, C::QNL, NW>(dvo, dsb, w, ln);
         const Rsrc qrs = make_rsrc(static_cast<const bf16*>(a.q) + b * a.sq.b + h * a.sq.h,
                                    rows_extent(p.N, qsb, 2 * D));
         const Rsrc drs = make_rsrc(static_cast<const bf16*>(a.dout) + b * a.sdo.b + h * a.sdo.h,
                                    rows_extent(p.N, dsb, 2 * D));
-        dma_tile<D, C::BQ>(qrs, qvo, (uint32_t)q0b * qsb, stage, w);
-        dma_tile<D, C::BQ>(drs, dvo, (uint32_t)q0b * dsb, stage + T::BYTES, w);
+        dma_tile<D, C::BQ, NW>(qrs, qvo, (uint32_t)q0b * qsb, stage, w);
+        dma_tile<D, C::BQ, NW>(drs, dvo, (uint32_t)q0b * dsb, stage + T::BYTES, w);
         if (w < 2) {  // wave-uniform: wave 0 loads LSE, wave 1 D
           const int64_t row0 = ((int64_t)b * p.Hq + h) * p.N;
           const Rsrc rs = make_rsrc((w ? a.dvec : a.lse2) + row0, (uint32_t)p.N * 4);
@@ -629,10 +637,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
         }
       };
       {
-        int vvo[VT::NLD];
-        dma_offsets_t<VT>(vvo, vsb, w, lane);
+        int vvo[C::VNL];
+        dma_offsets_t<VT, C::VNL, NW>(vvo, vsb, w, lane);
         const Rsrc vrs = make_rsrc(Vp, rows_extent(kvalid, vsb, 2 * D));
-        dma_tile<D, C::BK>(vrs, vvo, (uint32_t)k0 * vsb, smem + C::VOFF, w);
+        dma_tile<D, C::BK, NW>(vrs, vvo, (uint32_t)k0 * vsb, smem + C::VOFF, w);
       }
       // Row operands (query, dO and V rows 16 x + li, chunk 4 dc + lg; the
       // swizzle depends on a row's low 4 bits only, so the 16-row block
@@ -665,14 +673,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
           issue(nx, fill);
           paranoid_after_fill();
         }
-        if (a.log_kv && tid == 0)
-          log_tile(a.log_kv, (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw, k0);
+        if (a.log_kv && tid == 0) {
+          // Every 128-key block of the workgroup that a row of the step sees.
+          const int64_t row_word0 = (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw;
+          for (int kc = k0; kc < k0 + C::BK && kc < kvalid; kc += 128)
+            if (!causal || kc <= q0b + C::BQ - 1) log_tile(a.log_kv, row_word0, kc);
+        }
         const bool need_mask = (causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid);
-        // Causal pairs: when every row of the step lies above the wave's keys
-        // its P is exactly 0 and the step adds nothing to dK or dV.
-        const bool wave_off = NREP == 2 && q0b + C::BQ - 1 < kw0;
+        const char* Vw = Vb + 32 * w * VT::RB;
+        // 32-row sub-blocks of the step, one after the other (a loop, not
+        // unrolled: two unrolled copies would overlap and spill).
+#pragma unroll 1
+        for (int sb = 0; sb < C::NSB; ++sb) {
+        const int qs0 = q0b + 32 * sb;
+        const char* Qsb = Qs + 32 * sb * T::RB;
+        const char* dOsb = dOs + 32 * sb * T::RB;
+        // Causal pairs: when every row of the sub-block lies above the wave's
+        // keys its P is exactly 0 and it adds nothing to dK or dV.
+        const bool wave_off = NREP == 2 && qs0 + 31 < kw0;
         if (!wave_off) {
-          const char* Vw = Vb + 32 * w * VT::RB;
           int roff[C::NDC], toff[C::NDB];
           {
             int r0 = roff0, t0 = toff0;
@@ -693,8 +712,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
             bf16x8 qa[2], da[2], va[2];
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-              qa[x] = lds_row(Qs + 16 * x * T::RB, roff[dc]);
-              da[x] = lds_row(dOs + 16 * x * T::RB, roff[dc]);
+              qa[x] = lds_row(Qsb + 16 * x * T::RB, roff[dc]);
+              da[x] = lds_row(dOsb + 16 * x * T::RB, roff[dc]);
               va[x] = lds_row(Vw + 16 * x * VT::RB, roff[dc]);
             }
 #pragma unroll
@@ -718,12 +737,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
           }
           __builtin_amdgcn_s_setprio(0);
-          // LSE log2e and D of rows q0b + 16 rb + 4 lg + r, r = 0..3.
+          // LSE log2e and D of rows qs0 + 16 rb + 4 lg + r, r = 0..3.
           f32x4 l4[2], d4[2];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            l4[rb] = *reinterpret_cast<const f32x4*>(Qs + C::LSE_OFF + 4 * (16 * rb + 4 * lg));
-            d4[rb] = *reinterpret_cast<const f32x4*>(Qs + C::DVEC_OFF + 4 * (16 * rb + 4 * lg));
+            l4[rb] = *reinterpret_cast<const f32x4*>(Qs + C::LSE_OFF + 4 * (32 * sb + 16 * rb + 4 * lg));
+            d4[rb] = *reinterpret_cast<const f32x4*>(Qs + C::DVEC_OFF + 4 * (32 * sb + 16 * rb + 4 * lg));
           }
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
@@ -740,7 +759,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                   const int key = kw0 + 16 * kk + li;
-                  const int row = q0b + 16 * rb + 4 * lg + r;
+                  const int row = qs0 + 16 * rb + 4 * lg + r;
                   const bool kill = (causal && key > row) || key >= kvalid;
                   s[rb][kk][r] = kill ? 0.f : s[rb][kk][r];
                 }
@@ -758,8 +777,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
           __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const bf16x8 dot = lds_tr(dOs, toff[db], toff[db] + 16 * T::RB);
-            const bf16x8 qt = lds_tr(Qs, toff[db], toff[db] + 16 * T::RB);
+            const bf16x8 dot = lds_tr(dOsb, toff[db], toff[db] + 16 * T::RB);
+            const bf16x8 qt = lds_tr(Qsb, toff[db], toff[db] + 16 * T::RB);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
               dvt[db][kk] = mfma16(dot, pf[kk], dvt[db][kk]);
@@ -778,6 +797,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel_m16(BwdArgs a) {
           }
           __builtin_amdgcn_s_setprio(0);
         }  // !wave_off
+        }  // sub-blocks
         if (nx < nsteps) {
           wait_dma();
           __syncthreads();
@@ -1334,6 +1354,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel_m16(BwdArgs a) {
 #ifndef FA_DKDV_M16
 #define FA_DKDV_M16 1
 #endif
+#ifndef FA_DKDV_M16_WAVES
+#define FA_DKDV_M16_WAVES 8
+#endif
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t nkb = (a.p.N + 127) / 128;
@@ -1356,9 +1379,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
     if (a.p.drop) FA_DKDV_LAUNCH(64, true);
     else FA_DKDV_LAUNCH(64, false);
   } else if (!mask && FA_DKDV_M16) {
-    // Lean launches at d=128: the 16x16x32 kernel.
-    if (pair) hipLaunchKernelGGL((bwd_dkdv_kernel_m16<128, 2>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel_m16<128, 1>), g, blk, 0, s, a);
+    // Lean launches at d=128: the 16x16x32 kernel, 8 waves and 256 keys per
+    // workgroup.
+    constexpr int NW = FA_DKDV_M16_WAVES;
+    const int64_t nkb8 = (a.p.N + 32 * NW - 1) / (32 * NW);
+    const dim3 g8((unsigned)((pair ? (nkb8 + 1) / 2 : nkb8) * a.p.Hkv * a.p.B));
+    if (pair) hipLaunchKernelGGL((bwd_dkdv_kernel_m16<128, 2, NW>), g8, dim3(64 * NW), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel_m16<128, 1, NW>), g8, dim3(64 * NW), 0, s, a);
   } else {
     if (a.p.drop) FA_DKDV_LAUNCH(128, true);
     else FA_DKDV_LAUNCH(128, false);
