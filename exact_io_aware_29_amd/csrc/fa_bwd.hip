@@ -1089,19 +1089,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 //   dS^T = P (dP^T - D),  dQ^T += K^T dS^T   (K^T from transposing reads)
 // Each lane's accumulator registers of a 16x16 block all belong to the
 // lane's query row, so the dP^T chains start at that row's -D directly.
-template <int D>
+template <int D, int NW>
 struct DqM {
-  static constexpr int BR = 128;  // query rows per workgroup
-  static constexpr int BC = 64;   // keys per tile
+  // Query rows per workgroup: NW waves x 32. Keys per tile: 64 with 4 waves
+  // (two workgroups per CU); 128 with 8 waves (one workgroup per CU, still
+  // two waves per SIMD), which halves the barriers and the K/V DMA per
+  // product.
+  static constexpr int BR = 32 * NW;
+  static constexpr int BC = NW == 8 ? 128 : 64;
   static constexpr int NKB = BC / 16;
+  static constexpr int NH = BC / 32;  // 32-key halves per tile
   static constexpr int NDC = D / 32;
   static constexpr int NDB = D / 16;
   using T = SwzTile<D, BC, 1>;
+  static constexpr int KNL = T::BYTES / (NW * 1024);  // DMA loads per thread, K or V tile
 };
 
-template <int D, int NREP>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel_m16(BwdArgs a) {
-  using C = DqM<D>;
+template <int D, int NREP, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(BwdArgs a) {
+  using C = DqM<D, NW>;
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) char smem[2][2 * T::BYTES];
 
@@ -1184,9 +1190,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel_m16(BwdArgs a) {
       }
     }
 
-    int kvo[T::NLD], vvo[T::NLD];
-    dma_offsets_t<T>(kvo, ksb, w, lane);
-    dma_offsets_t<T>(vvo, vsb, w, lane);
+    int kvo[C::KNL], vvo[C::KNL];
+    dma_offsets_t<T, C::KNL, NW>(kvo, ksb, w, lane);
+    dma_offsets_t<T, C::KNL, NW>(vvo, vsb, w, lane);
     // Row operands (K and V rows 16 kb + li, chunk 4 dc + lg) and K^T
     // operands (transposing reads: key row 4 lg + e (+ 16, + 32 c) at
     // head-dim 16 db + 4 a for loader lane 4 e + a), as in the forward.
@@ -1208,11 +1214,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel_m16(BwdArgs a) {
 
     const int kend = causal ? min(kvalid, q0 + C::BR) : kvalid;
     const int ntiles = (kend + C::BC - 1) / C::BC;
-    const int64_t log_row =
-        a.log_q ? (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw : 0;
+    const int64_t log_row0 = (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw;
     auto issue = [&](int kt, char* stage) {
-      dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
-      dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
+      dma_tile<D, C::BC, NW>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
+      dma_tile<D, C::BC, NW>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
     };
     int kt = 0;
     if (kt < ntiles) {
@@ -1229,16 +1234,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel_m16(BwdArgs a) {
         issue(nxt, fill);
         paranoid_after_fill();
       }
-      if (a.log_q && tid == 0) log_tile(a.log_q, log_row, key0);
+      if (a.log_q && tid == 0) {
+        // Each 128-row block of the workgroup that sees a key of the tile.
+        for (int j = 0; j < C::BR / 128 && (q0 >> 7) + j < p.nlb; ++j)
+          if (!causal || key0 <= q0 + 128 * j + 127)
+            log_tile(a.log_q, log_row0 + (int64_t)j * p.logw, key0);
+      }
       const bool need_mask = (causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
       // Causal pairs: a wave whose rows all lie above the tile's keys has
       // P = 0 there and skips it (dQ bit-identical).
       const bool wave_off = NREP == 2 && key0 > r0 + 31;
       if (!wave_off) {
-        // Two 32-key halves, each S/dP -> P, dS -> dQ products, so that
-        // only half a tile of S and dP is live at once.
+        // 32-key halves, each S/dP -> P, dS -> dQ products, so that only
+        // half of a 64-key block of S and dP is live at once; a causal-pair
+        // wave skips a half whose keys all lie above its rows.
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < C::NH; ++c) {
+          if (NREP == 2 && C::NH > 2 && key0 + 32 * c > r0 + 31) continue;
           f32x4 s[2][2], dp[2][2];
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb)
@@ -1400,6 +1412,9 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
 #ifndef FA_DQ_M16_D64
 #define FA_DQ_M16_D64 1
 #endif
+#ifndef FA_DQ_M16_WIDE_N
+#define FA_DQ_M16_WIDE_N 8192
+#endif
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t grid = (int64_t)((a.p.N + 127) / 128) * a.p.Hq * a.p.B;
@@ -1419,13 +1434,22 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
     }                                                                                    \
   } while (0)
   if (!mask && FA_DQ_M16 && (head_dim == 128 || FA_DQ_M16_D64)) {
-    // Lean launches: the 16x16x32 kernel.
+    // Lean launches: the 16x16x32 kernel (4 waves at d=64, where 8 would
+    // lose a wave per SIMD).
     if (head_dim == 64) {
-      if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<64, 2>), g, blk, 0, s, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel_m16<64, 1>), g, blk, 0, s, a);
+      if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<64, 2, 4>), g, blk, 0, s, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel_m16<64, 1, 4>), g, blk, 0, s, a);
+    } else if (a.p.N >= FA_DQ_M16_WIDE_N) {
+      // Long rows: 256 query rows per workgroup. Below this length the
+      // larger causal diagonal block costs more than the halved barriers
+      // save (N = 4096: 0.668 -> 0.682 ms; N = 16384: 2.454 -> 2.381 ms).
+      const int64_t nqb8 = (a.p.N + 255) / 256;
+      const dim3 g8((unsigned)((pair ? (nqb8 + 1) / 2 : nqb8) * a.p.Hq * a.p.B));
+      if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 2, 8>), g8, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 1, 8>), g8, dim3(512), 0, s, a);
     } else {
-      if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 2>), g, blk, 0, s, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 1>), g, blk, 0, s, a);
+      if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 2, 4>), g, blk, 0, s, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 1, 4>), g, blk, 0, s, a);
     }
   } else if (head_dim == 64) {
     if (a.p.drop) FA_DQ_LAUNCH(64, true);

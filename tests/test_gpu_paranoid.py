@@ -44,6 +44,7 @@ CASES = [
     (1, 2, 2, 700, 128, False, "random", "butterfly", None, 0.0),
     (1, 2, 2, 333, 128, False, "random", None, None, 0.0),    # lean one-block, d=128
     (1, 4, 2, 520, 64, True, None, None, None, 0.0),           # lean causal pairs, d=64
+    (1, 2, 1, 8300, 128, True, "random", None, None, 0.0),    # long rows: 256-row dQ blocks
 ]
 
 

@@ -31,6 +31,8 @@ CASES = [
     (1, 2, 2, 1024, 64, False, None, "butterfly"),
     (2, 4, 4, 384, 128, True, [384, 130], "butterfly"),
     (1, 8, 2, 256, 128, False, None, None),
+    (1, 2, 1, 8300, 128, True, "random", None),   # long rows: the 256-row dQ blocks, ragged
+    (1, 1, 1, 8200, 128, False, None, None),
 ]
 
 # Sliding-window (local) attention: (case as above, (left, right) band).
