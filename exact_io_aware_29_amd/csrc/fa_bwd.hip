@@ -510,7 +510,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------- dK, dV, 16x16x32 products
 //
-// The lean dK/dV pass (no block mask, no window, no dropout) at d=128 on the
+// The dK/dV pass without a block mask or dropout (causal, key padding and
+// sliding windows allowed) at d=128 on the
 // 16x16x32 matrix instruction. Per wave two 16-key blocks (keys
 // k0 + 32 w + 16 kb + i), per step two 16-row query blocks:
 //   S = Q K^T    (A: query rows from the stage, B: the lane's key rows)
@@ -605,8 +606,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
       // Steps: (query head of the group) x (32-row query block), from the
       // causal diagonal down; query blocks from the last one, heads of the
       // group innermost.
-      const int qfirst = (causal ? k0 : 0) / C::BQ;
-      const int nq = (p.N + C::BQ - 1) / C::BQ - qfirst;
+      // Rows that can see a key of this block: from the causal diagonal or
+      // the right window edge, up to the left window edge.
+      const int qfirst = max(causal ? k0 : 0, k0 - p.wr) / C::BQ;
+      const int qend = min(p.N, k0 + C::BK + p.wl);
+      const int nq = max(0, (qend + C::BQ - 1) / C::BQ - qfirst);
       const int nsteps = p.G * nq;
       auto step_unit = [&](int sidx, int& h, int& q0b) {
         const int jd = p.G == 1 ? sidx : sidx / p.G;
@@ -676,10 +680,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
         if (a.log_kv && tid == 0) {
           // Every 128-key block of the workgroup that a row of the step sees.
           const int64_t row_word0 = (((int64_t)b * p.Hq + h) * p.nlb + (q0b >> 7)) * p.logw;
+          const int hi = causal ? 0 : p.wr;
           for (int kc = k0; kc < k0 + C::BK && kc < kvalid; kc += 128)
-            if (!causal || kc <= q0b + C::BQ - 1) log_tile(a.log_kv, row_word0, kc);
+            if (kc <= q0b + C::BQ - 1 + hi && kc + 127 >= q0b - p.wl)
+              log_tile(a.log_kv, row_word0, kc);
         }
-        const bool need_mask = (causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid);
+        // (Causal pairs never carry a window: its terms compile into the
+        // one-block instances only.)
+        const bool need_mask =
+            (causal && k0 + C::BK - 1 > q0b) || (k0 + C::BK > kvalid) ||
+            (NREP == 1 && ((q0b + C::BQ - 1 > k0 + p.wl) || (q0b < k0 + C::BK - 1 - p.wr)));
         const char* Vw = Vb + 32 * w * VT::RB;
         // 32-row sub-blocks of the step, one after the other (a loop, not
         // unrolled: two unrolled copies would overlap and spill).
@@ -688,9 +698,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
         const int qs0 = q0b + 32 * sb;
         const char* Qsb = Qs + 32 * sb * T::RB;
         const char* dOsb = dOs + 32 * sb * T::RB;
-        // Causal pairs: when every row of the sub-block lies above the wave's
-        // keys its P is exactly 0 and it adds nothing to dK or dV.
-        const bool wave_off = NREP == 2 && qs0 + 31 < kw0;
+        // When no row of the sub-block sees a key of the wave (above the
+        // causal diagonal, outside the band) its P is exactly 0 and it adds
+        // nothing to dK or dV.
+        const bool wave_off = NREP == 2 ? qs0 + 31 < kw0
+                                        : qs0 + 31 + (causal ? 0 : p.wr) < kw0 ||
+                                              qs0 - p.wl > kw0 + 31;
         if (!wave_off) {
           int roff[C::NDC], toff[C::NDB];
           {
@@ -752,6 +765,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
               for (int r = 0; r < 4; ++r)
                 s[rb][kk][r] = __builtin_amdgcn_exp2f(fmaf(s[rb][kk][r], sl2, -l4[rb][r]));
           if (__builtin_expect(need_mask, false)) {
+            const unsigned span = (unsigned)p.wl + (causal ? 0u : (unsigned)p.wr);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -760,7 +774,10 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
                 for (int r = 0; r < 4; ++r) {
                   const int key = kw0 + 16 * kk + li;
                   const int row = qs0 + 16 * rb + 4 * lg + r;
-                  const bool kill = (causal && key > row) || key >= kvalid;
+                  // Row i sees key j iff i - wl <= j <= i + hi (hi = 0 under
+                  // the causal mask, else the right window edge), j < kvalid.
+                  const bool kill = key >= kvalid || (NREP == 2 ? key > row
+                                                                : (unsigned)(key - row + p.wl) > span);
                   s[rb][kk][r] = kill ? 0.f : s[rb][kk][r];
                 }
           }
@@ -1081,7 +1098,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------- dQ, 16x16x32 products
 //
-// The lean dQ pass (no block mask, no window, no dropout) at d=128 on the
+// The dQ pass without a block mask or dropout (causal, key padding and
+// sliding windows allowed) on the
 // 16x16x32 matrix instruction (less energy per flop than 32x32x16 under the
 // board's power limit; see the forward's 16x16x32 kernel for the layouts).
 // Per wave two 16-row blocks; per 64-key tile four 16-key blocks:
@@ -1212,14 +1230,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(Bw
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) acc[db][0] = acc[db][1] = f32x4{};
 
-    const int kend = causal ? min(kvalid, q0 + C::BR) : kvalid;
+    // Keys any row of the block may see (causal / padding / right window
+    // edge bound the end, the left window edge the start).
+    const int kend = min(causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
     const int ntiles = (kend + C::BC - 1) / C::BC;
     const int64_t log_row0 = (((int64_t)b * p.Hq + h) * p.nlb + (q0 >> 7)) * p.logw;
     auto issue = [&](int kt, char* stage) {
       dma_tile<D, C::BC, NW>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
       dma_tile<D, C::BC, NW>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
     };
-    int kt = 0;
+    int kt = max(0, q0 - p.wl) / C::BC;
     if (kt < ntiles) {
       issue(kt, smem[0]);
       wait_dma();
@@ -1235,15 +1255,24 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(Bw
         paranoid_after_fill();
       }
       if (a.log_q && tid == 0) {
-        // Each 128-row block of the workgroup that sees a key of the tile.
-        for (int j = 0; j < C::BR / 128 && (q0 >> 7) + j < p.nlb; ++j)
-          if (!causal || key0 <= q0 + 128 * j + 127)
+        // Each 128-row block of the workgroup that sees a key of the tile:
+        // rows i of the block and keys j of the tile with i - wl <= j <=
+        // i + hi (hi = 0 under the causal mask, else the right window edge).
+        const int hi = causal ? 0 : p.wr;
+        for (int j = 0; j < C::BR / 128 && (q0 >> 7) + j < p.nlb; ++j) {
+          const int qj = q0 + 128 * j;
+          if (key0 <= qj + 127 + hi && key0 + C::BC - 1 >= qj - p.wl)
             log_tile(a.log_q, log_row0 + (int64_t)j * p.logw, key0);
+        }
       }
-      const bool need_mask = (causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
-      // Causal pairs: a wave whose rows all lie above the tile's keys has
-      // P = 0 there and skips it (dQ bit-identical).
-      const bool wave_off = NREP == 2 && key0 > r0 + 31;
+      const bool need_mask =
+          (causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
+          (NREP == 1 && ((key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr)));
+      // A wave whose rows see no key of the tile (above the causal diagonal,
+      // outside the band) has P = 0 there and skips it (dQ bit-identical).
+      const bool wave_off = NREP == 2 ? key0 > r0 + 31
+                                      : key0 > r0 + 31 + (causal ? 0 : p.wr) ||
+                                            key0 + C::BC - 1 < r0 - p.wl;
       if (!wave_off) {
         // 32-key halves, each S/dP -> P, dS -> dQ products, so that only
         // half of a 64-key block of S and dP is live at once; a causal-pair
@@ -1296,6 +1325,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(Bw
               for (int r = 0; r < 4; ++r)
                 s[hb][rb][r] = __builtin_amdgcn_exp2f(fmaf(s[hb][rb][r], sl2, -lse2[rb]));
           if (__builtin_expect(need_mask, false)) {
+            const unsigned span = (unsigned)p.wl + (causal ? 0u : (unsigned)p.wr);
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -1304,7 +1334,10 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(Bw
                 for (int r = 0; r < 4; ++r) {
                   const int key = key0 + 32 * c + 16 * hb + 4 * lg + r;
                   const int row = r0 + 16 * rb + li;
-                  const bool kill = (causal && key > row) || key >= kvalid;
+                  // Row i sees key j iff i - wl <= j <= i + hi (hi = 0 under
+                  // the causal mask, else the right window edge), j < kvalid.
+                  const bool kill = key >= kvalid || (NREP == 2 ? key > row
+                                                                : (unsigned)(key - row + p.wl) > span);
                   s[hb][rb][r] = kill ? 0.f : s[hb][rb][r];
                 }
           }
@@ -1390,9 +1423,9 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   if (head_dim == 64) {
     if (a.p.drop) FA_DKDV_LAUNCH(64, true);
     else FA_DKDV_LAUNCH(64, false);
-  } else if (!mask && FA_DKDV_M16) {
-    // Lean launches at d=128: the 16x16x32 kernel, 8 waves and 256 keys per
-    // workgroup.
+  } else if (a.p.bm == nullptr && !a.p.drop && FA_DKDV_M16) {
+    // No block mask or dropout at d=128 (causal, key padding and windows
+    // allowed): the 16x16x32 kernel, 8 waves and 256 keys per workgroup.
     constexpr int NW = FA_DKDV_M16_WAVES;
     const int64_t nkb8 = (a.p.N + 32 * NW - 1) / (32 * NW);
     const dim3 g8((unsigned)((pair ? (nkb8 + 1) / 2 : nkb8) * a.p.Hkv * a.p.B));
@@ -1433,16 +1466,19 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
       else hipLaunchKernelGGL((bwd_dq_kernel<DD, DR, 1, DR>), g, blk, 0, s, a);       \
     }                                                                                    \
   } while (0)
-  if (!mask && FA_DQ_M16 && (head_dim == 128 || FA_DQ_M16_D64)) {
-    // Lean launches: the 16x16x32 kernel (4 waves at d=64, where 8 would
-    // lose a wave per SIMD).
+  if (a.p.bm == nullptr && !a.p.drop && FA_DQ_M16 && (head_dim == 128 || FA_DQ_M16_D64)) {
+    // No block mask or dropout (causal, key padding and windows allowed):
+    // the 16x16x32 kernel (4 waves at d=64, where 8 would lose a wave per
+    // SIMD).
     if (head_dim == 64) {
       if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<64, 2, 4>), g, blk, 0, s, a);
       else hipLaunchKernelGGL((bwd_dq_kernel_m16<64, 1, 4>), g, blk, 0, s, a);
-    } else if (a.p.N >= FA_DQ_M16_WIDE_N) {
-      // Long rows: 256 query rows per workgroup. Below this length the
-      // larger causal diagonal block costs more than the halved barriers
-      // save (N = 4096: 0.668 -> 0.682 ms; N = 16384: 2.454 -> 2.381 ms).
+    } else if (a.p.N >= FA_DQ_M16_WIDE_N && a.p.wl >= a.p.N && a.p.wr >= a.p.N) {
+      // Long rows without a window: 256 query rows per workgroup. Below this
+      // length the larger causal diagonal block costs more than the halved
+      // barriers save (N = 4096: 0.668 -> 0.682 ms; N = 16384: 2.454 ->
+      // 2.381 ms); under a window the band's edge blocks do (N = 8192,
+      // 1023 keys back: 0.414 ms with 128 rows, 0.468 ms with 256).
       const int64_t nqb8 = (a.p.N + 255) / 256;
       const dim3 g8((unsigned)((pair ? (nqb8 + 1) / 2 : nqb8) * a.p.Hq * a.p.B));
       if (pair) hipLaunchKernelGGL((bwd_dq_kernel_m16<128, 2, 8>), g8, dim3(512), 0, s, a);

@@ -504,7 +504,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
 
 // ------------------------------------------------------ bf16, 16x16x32 MFMA
 //
-// The lean forward (no block mask, no window, no dropout) on the
+// The forward without a block mask or dropout (causal, key padding and
+// sliding windows allowed) on the
 // v_mfma_f32_16x16x32_bf16 matrix instruction. Under the board's power
 // limit a 16x16x32 product costs less energy per flop than a 32x32x16 one
 // (it moves a quarter of the accumulator registers for half the flops), and
@@ -571,7 +572,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
     }
     const int q0 = qb * C::BR;
     const int r0 = q0 + 32 * w;  // first row of this wave
-    const int kend = p.causal ? min(kvalid, q0 + C::BR) : kvalid;
+    // Keys any row of the block may see: causal / padding / right window
+    // edge bound the end, the left window edge the start.
+    const int kend = min(p.causal ? min(kvalid, q0 + C::BR) : kvalid, q0 + C::BR + p.wr);
     const int ntiles = (kend + C::BC - 1) / C::BC;
 
     // The lane's two query rows r0 + li and r0 + 16 + li as B operands:
@@ -621,7 +624,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
       dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
       dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
     };
-    int kt = 0;
+    int kt = max(0, q0 - p.wl) / C::BC;
     if (kt < ntiles) {
       issue(kt, smem[0]);
       wait_dma();
@@ -637,10 +640,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
         paranoid_after_fill();
       }
       if (a.log && tid == 0) log_tile(a.log, log_row, key0);
-      const bool need_mask = (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid);
-      // Causal pairs: a wave whose rows all lie above the tile's keys skips it
-      // (every score -inf, P~ = 0: m, l and O come out bit-identical).
-      const bool wave_off = NREP == 2 && key0 > r0 + 31;
+      // (Causal pairs never carry a window: its terms compile into the
+      // one-block instances only.)
+      const bool need_mask =
+          (p.causal && key0 + C::BC - 1 > q0) || (key0 + C::BC > kvalid) ||
+          (NREP == 1 && ((key0 < q0 + C::BR - 1 - p.wl) || (key0 + C::BC - 1 > q0 + p.wr)));
+      // A wave whose rows see no key of the tile (above the causal diagonal,
+      // outside the band) skips it: every score -inf, P~ = 0, and m, l and O
+      // come out bit-identical.
+      const bool wave_off = NREP == 2 ? key0 > r0 + 31
+                                      : key0 > r0 + 31 + (p.causal ? 0 : p.wr) ||
+                                            key0 + C::BC - 1 < r0 - p.wl;
       if (!wave_off) {
         f32x4 s[C::NKB][2];
 #pragma unroll
@@ -667,8 +677,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
         }
         __builtin_amdgcn_s_setprio(0);
         if (__builtin_expect(need_mask, false)) {
-          // Register r of key block kb is key key0 + 16 kb + 4 lg + r; row
-          // r0 + 16 rb + li sees keys up to itself (causal) below kvalid.
+          // Register r of key block kb is key key0 + 16 kb + 4 lg + r. Row i
+          // sees key j iff i - wl <= j <= i + hi (hi = 0 under the causal
+          // mask, else the right window edge) and j < kvalid: one unsigned
+          // compare of j - i + wl against wl + hi.
+          const unsigned span = (unsigned)p.wl + (p.causal ? 0u : (unsigned)p.wr);
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -677,7 +690,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
               for (int r = 0; r < 4; ++r) {
                 const int key = key0 + 16 * kb + 4 * lg + r;
                 const int row = r0 + 16 * rb + li;
-                const bool kill = (p.causal && key > row) || key >= kvalid;
+                const bool kill = key >= kvalid || (NREP == 2 ? key > row
+                                                              : (unsigned)(key - row + p.wl) > span);
                 s[kb][rb][r] = kill ? -kInf : s[kb][rb][r];
               }
         }
@@ -810,15 +824,19 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Lean launches (no mask, window or dropout) at d=128 take the 16x16x32
-// kernel; at d=64 the 32x32x16 kernel fits four waves per SIMD (the
-// 16x16x32 one needs 142 VGPRs there) and stays faster.
+// Launches without a block mask or dropout at d=128 (causal, key padding
+// and sliding windows allowed) take the 16x16x32 kernel; at d=64 the
+// 32x32x16 kernel fits four waves per SIMD (the 16x16x32 one needs 142
+// VGPRs there) and stays faster.
 template <int D, bool DROP, int NREP>
 static void launch_fwd_bf16_m(const FwdArgs& a, dim3 g, hipStream_t s) {
-  if (DROP || a.p.bm || a.p.wl < a.p.N || a.p.wr < a.p.N) {
+  const bool window = a.p.wl < a.p.N || a.p.wr < a.p.N;
+  if (DROP || a.p.bm) {
     hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, true>), g, dim3(256), 0, s, a);
   } else if constexpr (D == 128) {
     hipLaunchKernelGGL((fwd_kernel_m16<D, NREP>), g, dim3(256), 0, s, a);
+  } else if (window) {
+    hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, true>), g, dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL((fwd_kernel_bf16<D, DROP, NREP, DROP>), g, dim3(256), 0, s, a);
   }

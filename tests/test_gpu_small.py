@@ -43,6 +43,7 @@ WINDOW_CASES = [
     ((1, 2, 2, 640, 64, False, None, "random"), (130, 60)),
     ((1, 2, 2, 257, 64, True, None, None), (0, 0)),
     ((2, 4, 4, 384, 128, False, [384, 130], None), (0, 3)),
+    ((1, 2, 1, 8300, 128, True, None, None), (700, 0)),    # long rows: 256-row dQ blocks
 ]
 
 

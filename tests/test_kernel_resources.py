@@ -12,7 +12,9 @@ they are pinned here:
   VGPRs), and the bf16 forward at d=64 fits four (at most 128), which is
   what makes it fast; the fp32 reference-precision forward (a parity path)
   may take the whole 512;
-* static LDS of two resident workgroups fits the CU's 160 KiB.
+* static LDS of the resident workgroups that give two waves per SIMD fits
+  the CU's 160 KiB: two workgroups of 256 threads, or one of 512 (the
+  eight-wave dQ and dK/dV kernels).
 """
 import os
 import re
@@ -51,7 +53,8 @@ def _kernels(src: str):
             return m.group(1) if m else None
         ks.append({"name": field("name"), "vgpr": int(field("vgpr_count")),
                    "spill": int(field("vgpr_spill_count")),
-                   "lds": int(field("group_segment_fixed_size"))})
+                   "lds": int(field("group_segment_fixed_size")),
+                   "threads": int(field("max_flat_workgroup_size"))})
     assert ks, f"no kernel metadata found for {src}"
     return ks
 
@@ -66,7 +69,8 @@ def kernels():
 @needs_hipcc
 def test_every_source_has_kernels(kernels):
     names = [k["name"] for ks in kernels.values() for k in ks]
-    for stem in ("fwd_kernel_bf16", "fwd_kernel_fp8", "bwd_dkdv_kernel", "bwd_dq_kernel",
+    for stem in ("fwd_kernel_bf16", "fwd_kernel_m16", "fwd_kernel_fp8", "bwd_dkdv_kernel",
+                 "bwd_dkdv_kernel_m16", "bwd_dq_kernel", "bwd_dq_kernel_m16",
                  "decode_split_kernel", "decode_combine_kernel"):
         assert any(stem in n for n in names), stem
 
@@ -85,6 +89,10 @@ def test_occupancy_budgets(kernels):
         for k in ks:
             budget = 512 if "fwd_kernelIf" in k["name"] else 256
             assert k["vgpr"] <= budget, f"{k['name']}: {k['vgpr']} VGPRs"
-            assert 2 * k["lds"] <= 160 * 1024, f"{k['name']}: {k['lds']} bytes of LDS"
+            assert k["threads"] in (64, 256, 512), f"{k['name']}: {k['threads']} threads"
+            # Two waves per SIMD: two workgroups of 256 threads or one of 512
+            # (the 64-thread decode combine uses no LDS).
+            resident = 1 if k["threads"] == 512 else 2
+            assert resident * k["lds"] <= 160 * 1024, f"{k['name']}: {k['lds']} bytes of LDS"
             if "fwd_kernel_bf16ILi64ELb0ELi1E" in k["name"]:
                 assert k["vgpr"] <= 128, f"{k['name']}: {k['vgpr']} VGPRs (four waves need 128)"
