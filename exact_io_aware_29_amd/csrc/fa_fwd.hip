@@ -551,9 +551,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
   const int nqb = (p.N + C::BR - 1) / C::BR;
   static_assert(NREP == 1 || NREP == 2, "one block or a pair");
   const int nunit = NREP == 2 ? (nqb + 1) / 2 : nqb;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int head_lin = L / nunit;
-  const int ui = L - head_lin * nunit;
+  int head_lin, ui;
+  if (NREP == 1 && a.order) {
+    // Heaviest blocks first: block nqb - 1 - i / heads of head i mod heads.
+    // Workgroup i runs on XCD i mod 8, so with a head count divisible by 8
+    // every XCD keeps the same heads (and their K/V in its L2).
+    const int nh = p.Hq * p.B;
+    head_lin = (int)(blockIdx.x % (unsigned)nh);
+    ui = nqb - 1 - (int)(blockIdx.x / (unsigned)nh);
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    head_lin = L / nunit;
+    ui = L - head_lin * nunit;
+  }
   const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
 
   const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
@@ -842,13 +852,29 @@ static void launch_fwd_bf16_m(const FwdArgs& a, dim3 g, hipStream_t s) {
   }
 }
 
+#ifndef FA_FWD_HEAVY_FIRST_N
+#define FA_FWD_HEAVY_FIRST_N 8192
+#endif
+
 template <int D>
 static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const int64_t nqb = (a.p.N + FwdB<D>::BR - 1) / FwdB<D>::BR;
+  const bool causal_full = a.p.causal && a.p.wl >= a.p.N;
+  // Long causal rows at d = 128 (no block mask or dropout): single blocks,
+  // heaviest first. A mirror pair there is two blocks of up to N / 64 tiles,
+  // and the grid ends on a long tail of the last pairs; single blocks in
+  // decreasing size end on the lightest ones. At N = 4096 the pairs are
+  // short, and the single-block order measured no faster.
+  if (D == 128 && causal_full && !a.p.drop && !a.p.bm && a.p.N >= FA_FWD_HEAVY_FIRST_N) {
+    FwdArgs b = a;
+    b.order = 1;
+    launch_fwd_bf16_m<D, false, 1>(b, dim3((unsigned)(nqb * a.p.Hq * a.p.B)), s);
+    return hipGetLastError();
+  }
   // Pairs of query blocks where the work per block grows with the block
   // index (causal, no left window edge); under a sliding window every block
   // already does about the same work.
-  if (a.p.causal && a.p.wl >= a.p.N) {
+  if (causal_full) {
     const dim3 g((unsigned)(((nqb + 1) / 2) * a.p.Hq * a.p.B));
     if (a.p.drop) launch_fwd_bf16_m<D, true, 2>(a, g, s);
     else launch_fwd_bf16_m<D, false, 2>(a, g, s);

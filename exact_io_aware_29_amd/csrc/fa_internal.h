@@ -44,6 +44,10 @@ struct FwdArgs {
   int o_fp32;
   float qk_descale;  // FP8 inputs: descale_q * descale_k (scores) ...
   float v_descale;   // ... and descale_v (output)
+  // Grid order of one-block launches: 0 = head-major (XCD-remapped);
+  // 1 = heaviest blocks first, workgroup i taking block nqb - 1 - i / heads
+  // of head i mod heads (causal launches only).
+  int order = 0;
 };
 
 struct BwdArgs {
