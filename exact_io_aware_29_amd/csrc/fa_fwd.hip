@@ -553,12 +553,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
   const int nunit = NREP == 2 ? (nqb + 1) / 2 : nqb;
   int head_lin, ui;
   if (NREP == 1 && a.order) {
-    // Heaviest blocks first: block nqb - 1 - i / heads of head i mod heads.
-    // Workgroup i runs on XCD i mod 8, so with a head count divisible by 8
-    // every XCD keeps the same heads (and their K/V in its L2).
-    const int nh = p.Hq * p.B;
-    head_lin = (int)(blockIdx.x % (unsigned)nh);
-    ui = nqb - 1 - (int)(blockIdx.x / (unsigned)nh);
+    // Heaviest blocks first. Workgroup i runs on XCD i mod 8 and is that
+    // XCD's (i / 8)-th workgroup. With the key/value heads (b * Hkv + hk) a
+    // multiple of 8 in number, XCD x takes the heads congruent to x mod 8,
+    // block level by block level, the G query heads of each together, so
+    // each K/V head stays in one XCD's L2; otherwise workgroup i takes block
+    // nqb - 1 - i / heads of query head i mod heads.
+    const int ng = p.B * p.Hkv;
+    if ((ng & 7) == 0) {
+      const unsigned per = (unsigned)(ng >> 3) * (unsigned)p.G;  // items per level per XCD
+      const unsigned j = blockIdx.x >> 3;
+      const unsigned r = j % per;
+      const int grp = (int)(blockIdx.x & 7) + 8 * (int)(r / (unsigned)p.G);
+      head_lin = grp * p.G + (int)(r % (unsigned)p.G);
+      ui = nqb - 1 - (int)(j / per);
+    } else {
+      const int nh = p.Hq * p.B;
+      head_lin = (int)(blockIdx.x % (unsigned)nh);
+      ui = nqb - 1 - (int)(blockIdx.x / (unsigned)nh);
+    }
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     head_lin = L / nunit;
