@@ -14,7 +14,13 @@ they are pinned here:
   may take the whole 512;
 * static LDS of the resident workgroups that give two waves per SIMD fits
   the CU's 160 KiB: two workgroups of 256 threads, or one of 512 (the
-  eight-wave dQ and dK/dV kernels).
+  eight-wave dQ and dK/dV kernels);
+* scratch memory appears only in the documented VGPR-spilling instances;
+* scalar-register spills (to vector-register lanes, not memory) of the
+  instances the timed workloads run stay within the counts measured when
+  their speed was last checked. Re-reading the kernel arguments per block
+  cut the causal-pair dK/dV instance's 47 to 24 but made it 3-5% slower, so
+  these counts are a regression guard, not a target.
 """
 import os
 import re
@@ -53,6 +59,8 @@ def _kernels(src: str):
             return m.group(1) if m else None
         ks.append({"name": field("name"), "vgpr": int(field("vgpr_count")),
                    "spill": int(field("vgpr_spill_count")),
+                   "sspill": int(field("sgpr_spill_count")),
+                   "scratch": int(field("private_segment_fixed_size")),
                    "lds": int(field("group_segment_fixed_size")),
                    "threads": int(field("max_flat_workgroup_size"))})
     assert ks, f"no kernel metadata found for {src}"
@@ -81,6 +89,41 @@ def test_no_unexpected_spills(kernels):
         for k in ks:
             limit = next((lim for pat, lim in SPILL_ALLOWED if pat.search(k["name"])), 0)
             assert k["spill"] <= limit, f"{src}: {k['name']} spills {k['spill']} VGPRs"
+
+
+# Scalar spills allowed in the instances the timed workloads run (W2-W6:
+# the lean forward, dQ and dK/dV kernels), by mangled-name pattern.
+SCALAR_SPILL_MAX = [
+    (re.compile(r"fwd_kernel_m16ILi128ELi2E"), 0),                # W3 (causal pairs)
+    (re.compile(r"fwd_kernel_m16ILi128ELi1E"), 6),                # W4, W6
+    (re.compile(r"fwd_kernel_bf16ILi64ELb0ELi1ELb0E"), 0),        # W2
+    (re.compile(r"bwd_dq_kernel_m16ILi64ELi1ELi4E"), 0),          # W2
+    (re.compile(r"bwd_dq_kernel_m16ILi128ELi2ELi4E"), 4),         # W3
+    (re.compile(r"bwd_dq_kernel_m16ILi128ELi2ELi8E"), 11),        # W4
+    (re.compile(r"bwd_dq_kernel_m16ILi128ELi1ELi4E"), 0),         # W6
+    (re.compile(r"bwd_dkdv_kernel_m16ILi128ELi2ELi8E"), 47),      # W3, W4
+    (re.compile(r"bwd_dkdv_kernel_m16ILi128ELi1ELi8E"), 9),       # W6
+    (re.compile(r"bwd_dkdv_kernelILi64ELb0ELi1ELb0E"), 0),        # W2
+]
+
+
+@needs_hipcc
+def test_scratch_only_where_documented(kernels):
+    for src, ks in kernels.items():
+        for k in ks:
+            if any(pat.search(k["name"]) for pat, _ in SPILL_ALLOWED):
+                continue
+            assert k["scratch"] == 0, f"{src}: {k['name']} uses {k['scratch']} bytes of scratch"
+
+
+@needs_hipcc
+def test_scalar_spills_of_timed_instances(kernels):
+    names = [k["name"] for ks in kernels.values() for k in ks]
+    for pat, limit in SCALAR_SPILL_MAX:
+        hits = [k for ks in kernels.values() for k in ks if pat.search(k["name"])]
+        assert hits, f"no kernel matches {pat.pattern} among {len(names)}"
+        for k in hits:
+            assert k["sspill"] <= limit, f"{k['name']} spills {k['sspill']} SGPRs (limit {limit})"
 
 
 @needs_hipcc
