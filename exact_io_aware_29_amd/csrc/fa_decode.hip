@@ -117,8 +117,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
   auto issue = [&](int t, char* stage) {
     const uint32_t row0 = (uint32_t)(k_lo + t * C::BC);
-    dma_tile<D, C::BC>(krs, kvo, row0 * ksb, stage, w);
-    dma_tile<D, C::BC>(vrs, vvo, row0 * vsb, stage + T::BYTES, w);
+    // Every cache row is read once: non-temporal loads (5.46 -> 5.84 TB/s
+    // at B16 H32/KV8 with 16K-32K cached keys).
+    dma_tile<D, C::BC, 4, kCpolNonTemporal>(krs, kvo, row0 * ksb, stage, w);
+    dma_tile<D, C::BC, 4, kCpolNonTemporal>(vrs, vvo, row0 * vsb, stage + T::BYTES, w);
   };
   if (ntiles > 0) issue(0, smem[0]);
   wait_dma();

@@ -205,7 +205,13 @@ __device__ __forceinline__ void dma_offsets(int (&voff)[NL], int stride_bytes, i
   dma_offsets_t<SwzTile<D, ROWS>, NL, NW>(voff, stride_bytes, w, lane);
 }
 
-template <int D, int ROWS, int NW = 4>
+// Cache-policy bits of a buffer load (gfx950): non-temporal, for data
+// that is read once (evicted first rather than kept for reuse).
+constexpr int kCpolNonTemporal = 2;
+
+// CPOL: the loads' cache-policy bits (0 = default, for tiles that other
+// workgroups read again from L2; kCpolNonTemporal for a stream read once).
+template <int D, int ROWS, int NW = 4, int CPOL = 0>
 __device__ __forceinline__ void dma_tile(Rsrc rs, const int* voff, uint32_t soff, char* tile,
                                          int w) {
   using T = SwzTile<D, ROWS>;
@@ -213,7 +219,7 @@ __device__ __forceinline__ void dma_tile(Rsrc rs, const int* voff, uint32_t soff
 #pragma unroll
   for (int i = 0; i < NL; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + (i * NW + w) * 1024), 16,
-                                             voff[i], soff, 0, 0);
+                                             voff[i], soff, 0, CPOL);
 }
 
 // This wave's DMA loads have landed in LDS.
