@@ -68,6 +68,11 @@ def parse_args():
                     help="power analysis only: overwrite Q, K, V and dO with zeros or 0.5 "
                          "(same shapes, masks and kernels; the data field says so). The clock "
                          "follows board power, so timing depends on the data")
+    ap.add_argument("--timeline", action="store_true",
+                    help="instead of the benchmark line: time the workload with the release "
+                         "library, then with libfa_timeline.so (per-workgroup stamps in the "
+                         "16x16x32 kernels), and print one JSON line per stamped kernel: slot "
+                         "occupancy, time outside the tile loops, per-XCD speed and end times")
     ap.add_argument("--mix-ceiling", action="store_true",
                     help="instead of the benchmark: time the instruction-mix grid of "
                          "libfa_mixbench.so (64 matrix products per wave-tile with E "
@@ -463,6 +468,9 @@ def main():
     if w.decode:
         decode_main(args, w, inp, dev)
         return
+    if args.timeline:
+        timeline(args, w, inp, dev)
+        return
     rec = measure(args, args.workload, w, inp, dev, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         per_b = rec.pop("_per_b")
@@ -472,6 +480,87 @@ def main():
     if args.workload == 2 and not args.no_w3_record:
         rec["w3_record"] = w3_record(args, dev)
     print(json.dumps(rec), flush=True)
+
+
+TIMELINE_WORDS = 65536 * 16  # FA_TIMELINE_WORKGROUPS x FA_TIMELINE_SLOTS (include/fa_timeline.h)
+
+
+def timeline_stats(rows):
+    """Summary of one kernel launch's stamps (rows of workgroups that ran;
+    layout in include/fa_timeline.h). Times in microseconds."""
+    import numpy as np
+
+    us = 0.01  # the real-time counter runs at 100 MHz
+    t0 = rows[:, 0].min()
+    start, end = (rows[:, 0] - t0) * us, (rows[:, 10] - t0) * us
+    span = float(end.max())
+    xcc = (rows[:, 1] >> 32) & 0xF
+    loop = np.zeros(len(rows))
+    tiles = np.zeros(len(rows))
+    for r in range(2):
+        ran = rows[:, 2 + 4 * r] > 0
+        loop += np.where(ran, (rows[:, 4 + 4 * r] - rows[:, 3 + 4 * r]) * us, 0.0)
+        tiles += np.where(ran, rows[:, 5 + 4 * r] & 0xFFFF, 0)
+    grid = np.linspace(0.0, span, 401)
+    conc = np.array([((start <= t) & (end > t)).sum() for t in grid])
+    slots = int(conc.max())
+    busy = float((end - start).sum())
+    per_xcc_end = [float(end[xcc == x].max()) for x in range(8) if (xcc == x).any()]
+    per_xcc_rate = [float(loop[xcc == x].sum() / tiles[xcc == x].sum())
+                    for x in range(8) if tiles[xcc == x].sum() > 0]
+    return {
+        "workgroups": int(len(rows)),
+        "span_us": round(span, 1),
+        "resident_slots": slots,
+        "slot_occupancy": round(busy / (slots * span), 3),
+        "share_outside_tile_loop": round(1.0 - float(loop.sum()) / busy, 3),
+        "us_per_workgroup_tile": round(float(loop.sum() / tiles.sum()), 3),
+        "xcd_us_per_tile_min_max": [round(min(per_xcc_rate), 3), round(max(per_xcc_rate), 3)],
+        "xcd_end_us_min_max": [round(min(per_xcc_end), 1), round(max(per_xcc_end), 1)],
+        "last_start_us": round(float(start.max()), 1),
+    }
+
+
+def timeline(args, w, inp, dev):
+    """Time the workload with the release library, then with
+    libfa_timeline.so, and print one JSON line per stamped kernel with the
+    last launch's timeline summary and both libraries' kernel times (the
+    stamps perturb the kernels slightly; the release time is the reference)."""
+    import ctypes
+
+    import numpy as np
+
+    from exact_io_aware_29_amd import _abi
+
+    path = os.path.join(ROOT, "exact_io_aware_29_amd", "libfa_timeline.so")
+    release = measure(args, args.workload, w, inp, dev, args.steps, args.warmup)
+    raw = ctypes.CDLL(path)
+    raw.fa_timeline_fwd_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    raw.fa_timeline_bwd_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
+    saved = _abi.load()
+    _abi._lib = _abi.load_variant(path)
+    try:
+        for fn in (raw.fa_timeline_fwd_clear, raw.fa_timeline_bwd_clear):
+            if fn() != 0:
+                raise RuntimeError("clearing the timeline arrays failed")
+        stamped = measure(args, args.workload, w, inp, dev, args.steps, args.warmup)
+    finally:
+        _abi._lib = saved
+    for name, read in (("fwd", lambda b: raw.fa_timeline_fwd_read(b.ctypes.data, b.size)),
+                       ("bwd_dq", lambda b: raw.fa_timeline_bwd_read(0, b.ctypes.data, b.size)),
+                       ("bwd_dkdv", lambda b: raw.fa_timeline_bwd_read(1, b.ctypes.data, b.size))):
+        buf = np.zeros(TIMELINE_WORDS, dtype=np.uint64)
+        if read(buf) != 0:
+            raise RuntimeError(f"reading the {name} timeline failed")
+        rows = buf.reshape(-1, 16).astype(np.int64)
+        rows = rows[(rows[:, 0] > 0) & (rows[:, 10] > 0)]
+        if len(rows) == 0:
+            continue  # not a 16x16x32 kernel at this shape
+        rec = {"timeline": name, "workload": release["config"]["workload"],
+               "ms_release": release["kernels"][name]["ms"],
+               "ms_stamped": stamped["kernels"][name]["ms"]}
+        rec.update(timeline_stats(rows))
+        print(json.dumps(rec), flush=True)
 
 
 # Targets of the causal key-padded B8 H16 N4096 d128 configuration: the

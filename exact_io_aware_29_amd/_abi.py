@@ -80,6 +80,9 @@ SIGNATURES = {
 
 PARANOID_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                  "libfa_paranoid.so")
+# The debug build with per-workgroup timeline stamps (include/fa_timeline.h).
+TIMELINE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                 "libfa_timeline.so")
 
 _lib = None
 

@@ -48,6 +48,14 @@ PARANOID_OUT = os.path.join(PKG, "libfa_paranoid.so")
 PARANOID_FLAGS = ["-DFA_PARANOID_BARRIERS=1"]
 
 
+# Debug variant with per-workgroup timelines (FA_TIMELINE in fa_device.h):
+# the 16x16x32 forward, dQ and dK/dV kernels stamp entry, block, first-tile,
+# loop-end and exit times into device arrays that `bench.py --timeline`
+# reads (include/fa_timeline.h). Nothing else loads it.
+TIMELINE_OUT = os.path.join(PKG, "libfa_timeline.so")
+TIMELINE_FLAGS = ["-DFA_TIMELINE=1"]
+
+
 # Measurement only: the instruction-mix ceiling of the matrix-core kernels
 # (a grid of products / exponentials / other VALU mixes, timed by
 # ``bench.py --mix-ceiling``). The attention library does not load it.
@@ -68,7 +76,7 @@ def _compile(job) -> str:
     objdir = os.path.join(OBJDIR, variant) if variant else OBJDIR
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip", *KERNEL_FLAGS] if src.endswith(".hip") else []
-    extra = PARANOID_FLAGS if variant == "paranoid" else []
+    extra = {"paranoid": PARANOID_FLAGS, "timeline": TIMELINE_FLAGS}.get(variant, [])
     cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src),
            "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -118,20 +126,23 @@ def build_sanitized(verbose: bool = False):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libfa.so``, the debug variant
-    ``libfa_paranoid.so`` and the measurement library
-    ``libfa_mixbench.so``; returns the path of ``libfa.so``."""
+    """Compile every source and link ``libfa.so``, the debug variants
+    ``libfa_paranoid.so`` and ``libfa_timeline.so`` and the measurement
+    library ``libfa_mixbench.so``; returns the path of ``libfa.so``."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(os.path.join(OBJDIR, "paranoid"), exist_ok=True)
+    os.makedirs(os.path.join(OBJDIR, "timeline"), exist_ok=True)
+    n = len(SOURCES)
     jobs = ([(s, "") for s in SOURCES] + [(s, "paranoid") for s in SOURCES] +
-            [(MIXBENCH_SRC, "mixbench")])
+            [(s, "timeline") for s in SOURCES] + [(MIXBENCH_SRC, "mixbench")])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         objs = list(ex.map(_compile, jobs))
-    _link(objs[:len(SOURCES)], OUT)
-    _link(objs[len(SOURCES):2 * len(SOURCES)], PARANOID_OUT)
+    _link(objs[:n], OUT)
+    _link(objs[n:2 * n], PARANOID_OUT)
+    _link(objs[2 * n:3 * n], TIMELINE_OUT)
     if verbose:
-        print(f"built {OUT}, {PARANOID_OUT} and {MIXBENCH_OUT}")
+        print(f"built {OUT}, {PARANOID_OUT}, {TIMELINE_OUT} and {MIXBENCH_OUT}")
     build_sanitized(verbose)
     return OUT
 

@@ -522,6 +522,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 //   dV^T += dO^T P,   dK^T += Q^T dS   (A: two transposing reads, 4 rows each)
 // the slot order of the forward's P V product. The row statistics of those
 // four rows are one 16-byte LDS read per query block.
+#if FA_TIMELINE
+// Timeline stamps of the 16x16x32 dQ and dK/dV kernels (debug build).
+__device__ unsigned long long fa_tl_dq[kTlWorkgroups * kTlSlots];
+__device__ unsigned long long fa_tl_dkdv[kTlWorkgroups * kTlSlots];
+#endif
+
 template <int D, int NW>
 struct DkdvM {
   // Keys per workgroup: NW waves x 2 blocks of 16. Query rows per step: 32
@@ -572,6 +578,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
   const float sl2 = p.scale_l2;
   const bool causal = p.causal != 0;
   const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
+  FA_TL(fa_tl_dkdv, 0, tl_now());
+  FA_TL(fa_tl_dkdv, 1, tl_where());
   const int qsb = 2 * (int)a.sq.n, dsb = 2 * (int)a.sdo.n, vsb = 2 * (int)a.sv.n;
 
   for (int rep = 0; rep < NREP; ++rep) {
@@ -662,10 +670,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
         toff0 = rr * T::RB + 16 * ((d >> 3) ^ T::swz(rr)) + 2 * (d & 7);
       }
 
+      FA_TL(fa_tl_dkdv, 2 + 4 * rep, tl_now());
       int sidx = 0;
       if (sidx < nsteps) issue(sidx, smem);
       wait_dma();  // the V block and the first step
       __syncthreads();
+      FA_TL(fa_tl_dkdv, 3 + 4 * rep, tl_now());
       auto step = [&](const char* __restrict__ Qs, char* __restrict__ fill,
                       const char* __restrict__ Vb) {
         const char* dOs = Qs + T::BYTES;
@@ -823,6 +833,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
       };
       for (int st = 0; sidx < nsteps; st ^= 1)
         step(smem + st * C::STAGE, smem + (st ^ 1) * C::STAGE, smem + C::VOFF);
+      FA_TL(fa_tl_dkdv, 4 + 4 * rep, tl_now());
+      FA_TL(fa_tl_dkdv, 5 + 4 * rep, ((unsigned long long)kb << 16) | (unsigned)nsteps);
     }
 
     // Register e of block (db, kk) is head-dim 16 db + 4 lg + e of key
@@ -847,6 +859,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dkdv_kernel_m16(
       }
     }
   }  // key blocks of this workgroup
+  FA_TL(fa_tl_dkdv, 10, tl_now());
 }
 
 // ----------------------------------------------------------------- dQ
@@ -1141,6 +1154,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(Bw
   const int ui = L - head_lin * nunit;
   const int b = head_lin / p.Hq, h = head_lin - b * p.Hq, hk = h / p.G;
   const float sl2 = p.scale_l2;
+  FA_TL(fa_tl_dq, 0, tl_now());
+  FA_TL(fa_tl_dq, 1, tl_where());
   const bool causal = p.causal != 0;
 
   const int kvalid = __builtin_amdgcn_readfirstlane(valid_keys(p.seqlens, b, p.N));
@@ -1239,12 +1254,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(Bw
       dma_tile<D, C::BC, NW>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
       dma_tile<D, C::BC, NW>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
     };
+    FA_TL(fa_tl_dq, 2 + 4 * rep, tl_now());
     int kt = max(0, q0 - p.wl) / C::BC;
     if (kt < ntiles) {
       issue(kt, smem[0]);
       wait_dma();
       __syncthreads();
     }
+    FA_TL(fa_tl_dq, 3 + 4 * rep, tl_now());
     auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
       const char* Vs = Ks + T::BYTES;
       const int key0 = kt * C::BC;
@@ -1376,6 +1393,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(Bw
       kt = nxt;
     };
     for (int st = 0; kt < ntiles; st ^= 1) tile(smem[st], smem[st ^ 1]);
+    FA_TL(fa_tl_dq, 4 + 4 * rep, tl_now());
+    FA_TL(fa_tl_dq, 5 + 4 * rep, ((unsigned long long)qb << 16) | (unsigned)ntiles);
 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -1392,6 +1411,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void bwd_dq_kernel_m16(Bw
       }
     }
   }  // query blocks of this workgroup
+  FA_TL(fa_tl_dq, 10, tl_now());
 }
 
 // ----------------------------------------------------------------- launchers
@@ -1499,3 +1519,25 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
 }
 
 }  // namespace fa
+
+#if FA_TIMELINE
+// Debug build only (fa_timeline.h): copy or clear the dQ (which = 0) or
+// dK/dV (which = 1) stamps.
+extern "C" int fa_timeline_bwd_read(int which, void* dst, size_t words) {
+  if (words > (size_t)fa::kTlWorkgroups * fa::kTlSlots || which < 0 || which > 1) return -1;
+  return which ? (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(fa::fa_tl_dkdv), words * 8, 0,
+                                          hipMemcpyDeviceToHost)
+               : (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(fa::fa_tl_dq), words * 8, 0,
+                                          hipMemcpyDeviceToHost);
+}
+extern "C" int fa_timeline_bwd_clear() {
+  void* a = nullptr;
+  void* b = nullptr;
+  if (hipGetSymbolAddress(&a, HIP_SYMBOL(fa::fa_tl_dq)) != hipSuccess ||
+      hipGetSymbolAddress(&b, HIP_SYMBOL(fa::fa_tl_dkdv)) != hipSuccess)
+    return -1;
+  const size_t bytes = (size_t)fa::kTlWorkgroups * fa::kTlSlots * 8;
+  if (hipMemset(a, 0, bytes) != hipSuccess) return -1;
+  return (int)hipMemset(b, 0, bytes);
+}
+#endif

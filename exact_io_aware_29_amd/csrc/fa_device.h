@@ -138,6 +138,38 @@ __device__ __forceinline__ float tree_sum16(const f32x16& s) {
 // True in every lane if `pred` holds in any active lane of the wave.
 __device__ __forceinline__ bool wave_any(bool pred) { return __any(pred); }
 
+// Debug build with per-workgroup timelines (FA_TIMELINE=1, libfa_timeline.so;
+// nothing else loads it). Thread 0 of each workgroup stores 64-bit stamps
+// into a device array of its kernel: the 100 MHz real-time counter at fixed
+// points (entry, each block's start, its first tile or step ready, the end
+// of its tile loop, exit), the XCD / CU it runs on, and the block's tile
+// count. Only the first kTlWorkgroups workgroups of a launch record. In the
+// release build every stamp compiles to nothing.
+#ifndef FA_TIMELINE
+#define FA_TIMELINE 0
+#endif
+constexpr int kTlWorkgroups = 1 << 16;
+constexpr int kTlSlots = 16;  // words per workgroup
+// Word layout: 0 entry, 1 (XCC_ID << 32 | HW_ID), 10 exit; for block r of
+// the workgroup (r = 0, 1): 2 + 4r start, 3 + 4r first tile ready, 4 + 4r
+// tile loop done, 5 + 4r (block index << 16 | tiles or steps).
+#if FA_TIMELINE
+#define FA_TL(buf, slot, value)                                                   \
+  do {                                                                           \
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kTlWorkgroups)                \
+      (buf)[(size_t)blockIdx.x * kTlSlots + (slot)] = (unsigned long long)(value); \
+  } while (0)
+#else
+#define FA_TL(buf, slot, value) \
+  do {                          \
+  } while (0)
+#endif
+__device__ __forceinline__ unsigned long long tl_now() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ unsigned long long tl_where() {
+  return (unsigned long long)(unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 4) |
+         ((unsigned long long)(unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 20) << 32);
+}
+
 // Workgroup index -> logical index. Workgroups are handed to the 8 XCDs of
 // the chip round-robin (w % 8); this bijection gives each XCD a contiguous
 // range of logical indices, so the Q blocks of one head (adjacent logical

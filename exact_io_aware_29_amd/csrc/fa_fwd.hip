@@ -526,6 +526,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(FwdArgs a) {
 // over the 4 lanes i, i + 16, i + 32, i + 48: the row maximum and the row
 // sum finish with two lane swaps (permlane16 and permlane32).
 
+#if FA_TIMELINE
+// Timeline stamps of the 16x16x32 forward (debug build).
+__device__ unsigned long long fa_tl_fwd[kTlWorkgroups * kTlSlots];
+#endif
+
 template <int D>
 struct FwdM {
   static constexpr int BR = 128;    // rows per workgroup (4 waves x 2 blocks of 16)
@@ -586,6 +591,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
   const Rsrc vrs = make_rsrc(static_cast<const bf16*>(a.v) + b * a.sv.b + hk * a.sv.h,
                              rows_extent(kvalid, vsb, 2 * D));
   const float sl2 = p.scale_l2;
+  FA_TL(fa_tl_fwd, 0, tl_now());
+  FA_TL(fa_tl_fwd, 1, tl_where());
 
   for (int rep = 0; rep < NREP; ++rep) {
     const int qb = NREP == 2 ? (rep == 0 ? nqb - 1 - ui : ui) : ui;
@@ -647,12 +654,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
       dma_tile<D, C::BC>(krs, kvo, (uint32_t)(kt * C::BC) * ksb, stage, w);
       dma_tile<D, C::BC>(vrs, vvo, (uint32_t)(kt * C::BC) * vsb, stage + T::BYTES, w);
     };
+    FA_TL(fa_tl_fwd, 2 + 4 * rep, tl_now());
     int kt = max(0, q0 - p.wl) / C::BC;
     if (kt < ntiles) {
       issue(kt, smem[0]);
       wait_dma();
       __syncthreads();
     }
+    FA_TL(fa_tl_fwd, 3 + 4 * rep, tl_now());
     auto tile = [&](const char* __restrict__ Ks, char* __restrict__ fill) {
       const char* Vs = Ks + T::BYTES;
       const int key0 = kt * C::BC;
@@ -804,6 +813,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
       if (kt >= ntiles) break;
       tile(smem[1], smem[0]);
     }
+    FA_TL(fa_tl_fwd, 4 + 4 * rep, tl_now());
+    FA_TL(fa_tl_fwd, 5 + 4 * rep, ((unsigned long long)qb << 16) | (unsigned)ntiles);
 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -836,6 +847,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_m16(FwdArgs a) {
       }
     }
   }  // q-blocks of this workgroup
+  FA_TL(fa_tl_fwd, 10, tl_now());
 }
 
 // fp32 inputs (reference-precision path) use the generic kernel above.
@@ -907,3 +919,17 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, hipStream_t s) 
 }
 
 }  // namespace fa
+
+#if FA_TIMELINE
+// Debug build only (fa_timeline.h): copy or clear the forward's stamps.
+extern "C" int fa_timeline_fwd_read(void* dst, size_t words) {
+  if (words > (size_t)fa::kTlWorkgroups * fa::kTlSlots) return -1;
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(fa::fa_tl_fwd), words * 8, 0,
+                                  hipMemcpyDeviceToHost);
+}
+extern "C" int fa_timeline_fwd_clear() {
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(fa::fa_tl_fwd)) != hipSuccess) return -1;
+  return (int)hipMemset(ptr, 0, (size_t)fa::kTlWorkgroups * fa::kTlSlots * 8);
+}
+#endif

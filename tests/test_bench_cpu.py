@@ -99,3 +99,53 @@ def test_mixbench_library_exports_its_entry_points():
     assert lib.fa_mixbench(0, -1, 0, 1, 1, ctypes.byref(ms)) == -1
     assert lib.fa_mixbench(0, 0, 3, 1, 1, ctypes.byref(ms)) == -1
     assert lib.fa_mixbench(0, 0, 0, 0, 1, ctypes.byref(ms)) == -1
+
+
+def test_timeline_library_exports_its_entry_points_and_release_does_not():
+    """libfa_timeline.so (the stamped debug build) exports the four
+    fa_timeline_* calls of include/fa_timeline.h; libfa.so exports none.
+    Only symbol lookups here, no GPU call."""
+    import ctypes
+
+    pkg = os.path.join(ROOT, "exact_io_aware_29_amd")
+    names = ("fa_timeline_fwd_read", "fa_timeline_fwd_clear", "fa_timeline_bwd_read",
+             "fa_timeline_bwd_clear")
+    tl = ctypes.CDLL(os.path.join(pkg, "libfa_timeline.so"))
+    for n in names:
+        assert hasattr(tl, n), n
+    rel = ctypes.CDLL(os.path.join(pkg, "libfa.so"))
+    for n in names:
+        assert not hasattr(rel, n), n
+    assert bench.TIMELINE_WORDS == 65536 * 16
+
+
+def _timeline_rows():
+    """Four workgroups on two XCDs, two per XCD, in one slot each, stamped in
+    100 MHz ticks: entry, first tile ready, loop end and exit of one block
+    (word 5 = tiles), XCC id in word 1's high half."""
+    rows = np.zeros((4, 16), dtype=np.int64)
+    # (xcc, entry, block start, first tile, loop end, tiles, exit) in ticks
+    spec = [(0, 100, 110, 200, 1200, 10, 1300),
+            (0, 1300, 1310, 1400, 2400, 10, 2500),
+            (1, 100, 110, 200, 1700, 10, 1800),
+            (1, 1800, 1810, 1900, 3400, 10, 3500)]
+    for i, (x, e, s, f, l, t, q) in enumerate(spec):
+        rows[i, [0, 2, 3, 4, 5, 10]] = [e, s, f, l, t, q]
+        rows[i, 1] = (x << 32) | 7
+    return rows
+
+
+def test_timeline_stats_on_a_hand_made_launch():
+    st = bench.timeline_stats(_timeline_rows())
+    # span: first entry at 100 ticks, last exit at 3500 ticks -> 34 us
+    assert st["span_us"] == 34.0
+    assert st["workgroups"] == 4 and st["resident_slots"] == 2
+    # busy: 12 + 12 + 17 + 17 = 58 us of 2 x 34 us
+    assert st["slot_occupancy"] == round(58 / 68, 3)
+    # loop time: 10 + 10 + 15 + 15 = 50 us of 58 busy
+    assert st["share_outside_tile_loop"] == round(1 - 50 / 58, 3)
+    assert st["us_per_workgroup_tile"] == round(50 / 40, 3)
+    # XCD 0 runs 1.0 us per tile and ends at 24 us; XCD 1 1.5 us, 34 us
+    assert st["xcd_us_per_tile_min_max"] == [1.0, 1.5]
+    assert st["xcd_end_us_min_max"] == [24.0, 34.0]
+    assert st["last_start_us"] == 17.0

@@ -4,8 +4,11 @@ right after it) must give results bit-identical to the release build, which
 overlaps each refill with the reads of the other stage (Report section 3.2:
 K_j and V_j are staged tile by tile). A read that the release build let run
 ahead of a refill it depends on, or a refill that overwrote a stage still
-being read, would show here as a difference."""
+being read, would show here as a difference. The timeline build
+(libfa_timeline.so), which only adds timestamp stores, is held to the same
+bar on the paths that carry the stamps."""
 import contextlib
+import os
 
 import numpy as np
 import pytest
@@ -20,14 +23,18 @@ pytestmark = pytest.mark.gpu
 
 
 @contextlib.contextmanager
-def _paranoid():
-    """Route the binding's calls to the debug build for the duration."""
+def _variant(path):
+    """Route the binding's calls to another build for the duration."""
     saved = _abi.load()
-    _abi._lib = _abi.load_variant(_abi.PARANOID_LIB_PATH)
+    _abi._lib = _abi.load_variant(path)
     try:
         yield
     finally:
         _abi._lib = saved
+
+
+def _paranoid():
+    return _variant(_abi.PARANOID_LIB_PATH)
 
 
 def _bits(t):
@@ -52,8 +59,24 @@ CASES = [
                          f"{'c' if c[5] else ''}{'p' if c[6] is not None else ''}{c[7] or ''}"
                          f"{'w' if c[8] else ''}{'drop' if c[9] else ''}")
 def test_paranoid_build_is_bit_identical(case):
+    _compare_with(_abi.PARANOID_LIB_PATH, case)
+
+
+# The timeline build's stamps sit in the 16x16x32 kernels: their paths.
+TIMELINE_CASES = [CASES[0], CASES[3], CASES[6], CASES[7], CASES[8]]
+
+
+@pytest.mark.parametrize("case", TIMELINE_CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}N{c[3]}d{c[4]}"
+                         f"{'c' if c[5] else ''}{'w' if c[8] else ''}")
+def test_timeline_build_is_bit_identical(case):
+    """libfa_timeline.so only adds stores of timestamps: its results equal
+    the release build's bit for bit."""
+    _compare_with(_abi.TIMELINE_LIB_PATH, case)
+
+
+def _compare_with(path, case):
     B, Hq, Hkv, N, d, causal, sl, bm, window, p = case
-    print(f"paranoid vs release {case}", flush=True)
+    print(f"{os.path.basename(path)} vs release {case}", flush=True)
     inp = draw_case(B, Hq, Hkv, N, d, "bf16", causal=causal, seqlens=sl, block_mask=bm,
                     seed=N + 3 * d, window=window)
     q, k, v, do = (dev(getattr(inp, n), "bf16") for n in ("q", "k", "v", "do"))
@@ -70,7 +93,7 @@ def test_paranoid_build_is_bit_identical(case):
         return [o, lse, flog, o32, lse32, dq, dk, dv, blog]
 
     rel = run()
-    with _paranoid():
+    with _variant(path):
         par = run()
     names = ["O", "LSE", "fwd tiles", "O fp32", "LSE (fp32 O)", "dQ", "dK", "dV", "bwd tiles"]
     for name, a, b in zip(names, rel, par):
