@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import exact_io_aware_29_amd as fa
-from synth import WORKLOADS, draw
+from synth import WORKLOADS, Workload, draw
 from tests.gpu_util import (BF16_HALF_ULP_REL, TOL_BF16_LSE, TOL_BF16_O_ABS, TOL_FP32_LSE,
                             TOL_FP32_O, check_grad, check_lse, check_o, decode_log, dev,
                             expected_tiles, host64, oracle_heads)
@@ -25,10 +25,10 @@ from tests.gpu_util import (BF16_HALF_ULP_REL, TOL_BF16_LSE, TOL_BF16_O_ABS, TOL
 pytestmark = pytest.mark.gpu
 
 
-def _run(wid):
-    w = WORKLOADS[wid]
+def _run(wid, w=None, seed=None):
+    w = WORKLOADS[wid] if w is None else w
     print(f"workload {wid}: {w.describe()}", flush=True)
-    inp = draw(w, wid)
+    inp = draw(w, wid if seed is None else seed)
     q, k, v = dev(inp.q, w.dtype), dev(inp.k, w.dtype), dev(inp.v, w.dtype)
     sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).cuda()
     bm = None if inp.block_mask is None else torch.from_numpy(inp.block_mask).cuda()
@@ -186,3 +186,32 @@ def test_workload6_sliding_window():
                                        rng.integers(0, N, 40)]))
     k_rows = np.concatenate([np.arange(0, 8), np.arange(4090, 4100), np.arange(N - 8, N)])
     _compare(res, [(0, 0), (3, 15)], q_rows=q_rows, k_rows=k_rows)
+
+
+# Causal d=128 forwards of N >= 8192 without dropout or a block mask run one
+# query block per workgroup, heaviest blocks first. Workgroup i goes to XCD
+# i mod 8; when B * Hkv is a multiple of 8, each XCD takes whole GQA groups
+# (all G query heads of a K/V head, across batches), else the order is
+# head-major. Both branches, a ragged last block and key padding, each checked
+# through the tile log (every block's tiles exactly once, as the mask allows)
+# and oracle parity on the first, a middle and the last query head.
+HEAVY_FIRST_CASES = [
+    ("fallback", Workload("t", 1, 3, 3, 8192, 128, "bf16", causal=True, backward=False)),
+    ("grouped_b2_keypad", Workload("t", 2, 8, 4, 8192, 128, "bf16", causal=True,
+                                   pad_range=(5000, 8192), backward=False)),
+    ("grouped_ragged", Workload("t", 1, 16, 8, 8200, 128, "bf16", causal=True, backward=False)),
+]
+
+
+@pytest.mark.parametrize("name,w", HEAVY_FIRST_CASES, ids=[c[0] for c in HEAVY_FIRST_CASES])
+def test_heaviest_first_forward_orders(name, w):
+    res = _run(f"-{name}", w=w, seed=8192)
+    _check_tiles(res)
+    _check_invariants(res)
+    N = w.seqlen
+    rng = np.random.default_rng(81)
+    q_rows = np.unique(np.concatenate([np.arange(64), [127, 128, 4095, 4096, 8191],
+                                       np.arange(N - 24, N), rng.integers(0, N, 24)]))
+    last = (w.batch - 1, w.heads_q - 1)
+    heads = sorted({(0, 0), (w.batch // 2, w.heads_q // 2), last})
+    _compare(res, heads, q_rows=q_rows)
